@@ -1,0 +1,17 @@
+"""extreme_bit_kv_amd — the CalibQuant visual-KV decode path on MI355X (gfx950).
+
+Channel-wise b-bit quantization of the visual KV cache, post-scaled decode
+attention over the packed codes with the calibration map g, and an
+unquantized float16 decode baseline, all as hand-written HIP kernels behind
+the C ABI in include/cq.h (libcq.so).  This package is the thin Python
+binding over that library; see ``_binding`` for the functions.
+"""
+from ._binding import (CQ_F16, CQ_F32, CQ_LAYOUT_K, CQ_LAYOUT_V, CQ_PATH_AUTO, CQ_PATH_FAST,
+                       CQ_PATH_GENERIC, EXPORTED, LIB_PATH, CQError, code_words_shape, cq_calib,
+                       cq_calibrate, cq_decode_attn, cq_decode_attn_fp16, cq_opts, cq_quantize_kv, lib,
+                       make_calib)
+
+__all__ = ["CQ_F16", "CQ_F32", "CQ_LAYOUT_K", "CQ_LAYOUT_V", "CQ_PATH_AUTO", "CQ_PATH_FAST",
+           "CQ_PATH_GENERIC", "EXPORTED", "LIB_PATH", "CQError", "code_words_shape", "cq_calib",
+           "cq_calibrate", "cq_decode_attn", "cq_decode_attn_fp16", "cq_opts", "cq_quantize_kv", "lib",
+           "make_calib"]

@@ -1,0 +1,180 @@
+// C ABI of libcq: argument validation, path selection, workspace carving and
+// launches.  Every entry point validates before enqueuing anything, returns a
+// cq_status and never throws.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <cstdlib>
+
+#include "../../include/cq.h"
+#include "cq_internal.h"
+
+namespace {
+
+bool valid_bits(int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; }
+bool valid_dtype(int32_t t) { return t == CQ_F16 || t == CQ_F32; }
+int opt_path(const cq_opts* o) { return o ? o->path : CQ_PATH_AUTO; }
+
+thread_local int32_t g_last_hip_error = 0;
+
+cq_status from_hip(hipError_t e) {
+  if (e == hipSuccess) return CQ_OK;
+  g_last_hip_error = (int32_t)e;
+  return CQ_ERR_HIP;
+}
+
+// A HIP error left pending by earlier, unrelated calls of the same thread
+// (for instance from the framework that owns the tensors) must not be
+// reported as a failure of this library's launches.
+void clear_stale_hip_error() { (void)hipGetLastError(); }
+
+// Size of a tensor of `count` elements must fit a signed 64-bit byte count
+// and every per-(batch, head) index the kernels form in 32 bits.
+bool fits(int64_t a, int64_t b, int64_t c, int64_t d) {
+  if (a < 0 || b < 0 || c < 0 || d < 0) return false;
+  const int64_t lim = (int64_t)1 << 31;
+  if (c * d >= lim) return false;                       // per-unit element count
+  return a * b < lim;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t cq_abi_version(void) { return CQ_ABI_VERSION; }
+
+int32_t cq_last_hip_error(void) { return g_last_hip_error; }
+
+const char* cq_status_str(cq_status s) {
+  switch (s) {
+    case CQ_OK: return "CQ_OK";
+    case CQ_ERR_INVALID_ARG: return "CQ_ERR_INVALID_ARG: invalid argument";
+    case CQ_ERR_UNSUPPORTED: return "CQ_ERR_UNSUPPORTED: valid arguments not supported by this build";
+    case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE: workspace missing or too small";
+    case CQ_ERR_HIP: return "CQ_ERR_HIP: HIP runtime call failed";
+  }
+  return "unknown cq_status";
+}
+
+// ---------------------------------------------------------------------------
+size_t cq_quantize_kv_workspace(int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits) {
+  if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits)) return 0;
+  size_t g = cqi::quant_generic_ws(B, H, n, d);
+  size_t f = cqi::quant_fused_ws(B, H, n, d);
+  return g > f ? g : f;
+}
+
+cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, int32_t n, int32_t d,
+                         int32_t bits, cq_layout layout, uint32_t* codes, float* scale, float* minv,
+                         void* workspace, size_t workspace_bytes, const cq_opts* opts, void* stream) {
+  if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype) ||
+      (layout != CQ_LAYOUT_K && layout != CQ_LAYOUT_V))
+    return CQ_ERR_INVALID_ARG;
+  if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
+  const int path = opt_path(opts);
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST) return CQ_ERR_INVALID_ARG;
+  const int64_t units = (int64_t)B * H;
+  if (units > 0) {
+    if (scale == nullptr || minv == nullptr) return CQ_ERR_INVALID_ARG;
+    if (n > 0 && (x == nullptr || codes == nullptr)) return CQ_ERR_INVALID_ARG;
+  }
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  cqi::QuantArgs a{x, x_dtype, B, H, n, d, bits, layout, codes, scale, minv, workspace, (hipStream_t)stream};
+  const bool fused_ok = cqi::quant_fused_supported(a);
+  if (path == CQ_PATH_FAST && !fused_ok) return CQ_ERR_UNSUPPORTED;
+  const bool use_fused = fused_ok && path != CQ_PATH_GENERIC;
+  const size_t need = use_fused ? cqi::quant_fused_ws(B, H, n, d) : cqi::quant_generic_ws(B, H, n, d);
+  if (need > 0 && units > 0 && n > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
+  clear_stale_hip_error();
+  return from_hip(use_fused ? cqi::quant_fused(a) : cqi::quant_generic(a));
+}
+
+// ---------------------------------------------------------------------------
+size_t cq_decode_attn_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t T, int32_t d,
+                                int32_t bits) {
+  if (!fits(B, Hq, n, d) || !fits(B, Hkv, T, d) || Hkv <= 0 || Hq % Hkv != 0 || !valid_bits(bits)) return 0;
+  // enough for any split count a caller may request (the path clamps it)
+  int S = cqi::decode_generic_splits(n, B * Hkv, 1 << 30);
+  size_t g = cqi::decode_generic_ws(B, Hq, Hkv, n, T, d, S);
+  size_t f = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
+  return g > f ? g : f;
+}
+
+cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
+                         const float* k_min, const uint32_t* v_codes, const float* v_scale, const float* v_min,
+                         const void* k_tail, const void* v_tail, cq_dtype tail_dtype, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t n, int32_t T, int32_t d, int32_t bits, float sm_scale,
+                         const cq_calib* calib, void* out, cq_dtype out_dtype, void* workspace,
+                         size_t workspace_bytes, const cq_opts* opts, void* stream) {
+  if (!fits(B, Hq, n, d) || !fits(B, Hkv, T, d) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || d <= 0 ||
+      !valid_bits(bits) || !valid_dtype(q_dtype) || !valid_dtype(out_dtype) || !valid_dtype(tail_dtype))
+    return CQ_ERR_INVALID_ARG;
+  if ((d * bits) % 32 != 0 || n + (int64_t)T < 1) return CQ_ERR_INVALID_ARG;
+  if (!(sm_scale == sm_scale)) return CQ_ERR_INVALID_ARG;
+  const int path = opt_path(opts);
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST || (opts && opts->splits < 0)) return CQ_ERR_INVALID_ARG;
+  if (B > 0) {
+    if (q == nullptr || out == nullptr) return CQ_ERR_INVALID_ARG;
+    if (n > 0 && (k_codes == nullptr || k_scale == nullptr || k_min == nullptr || v_codes == nullptr ||
+                  v_scale == nullptr || v_min == nullptr))
+      return CQ_ERR_INVALID_ARG;
+    if (T > 0 && (k_tail == nullptr || v_tail == nullptr)) return CQ_ERR_INVALID_ARG;
+  }
+  if (T == 0 && (k_tail != nullptr || v_tail != nullptr)) return CQ_ERR_INVALID_ARG;
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return CQ_ERR_UNSUPPORTED;
+  cqi::DecodeArgs a{};
+  a.q = q; a.q_dtype = q_dtype;
+  a.k_codes = k_codes; a.k_scale = k_scale; a.k_min = k_min;
+  a.v_codes = v_codes; a.v_scale = v_scale; a.v_min = v_min;
+  a.k_tail = k_tail; a.v_tail = v_tail; a.tail_dtype = tail_dtype;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.T = T; a.d = d; a.bits = bits;
+  a.sm_scale = sm_scale;
+  a.calib_on = (calib != nullptr && calib->enabled) ? 1 : 0;
+  if (a.calib_on) { a.a_lo = calib->a_lo; a.c_lo = calib->c_lo; a.a_hi = calib->a_hi; a.c_hi = calib->c_hi; }
+  a.out = out; a.out_dtype = out_dtype;
+  a.ws = workspace;
+  a.splits = opts ? opts->splits : 0;
+  a.stream = (hipStream_t)stream;
+  const bool fast_ok = cqi::decode_fast_supported(a);
+  if (path == CQ_PATH_FAST && !fast_ok) return CQ_ERR_UNSUPPORTED;
+  const bool use_fast = fast_ok && path != CQ_PATH_GENERIC && !(opts && opts->splits > 0);
+  size_t need;
+  if (use_fast) need = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
+  else need = cqi::decode_generic_ws(B, Hq, Hkv, n, T, d, cqi::decode_generic_splits(n, B * Hkv, a.splits));
+  if (B > 0 && need > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
+  clear_stale_hip_error();
+  return from_hip(use_fast ? cqi::decode_fast(a) : cqi::decode_generic(a));
+}
+
+// ---------------------------------------------------------------------------
+cq_status cq_calibrate(const float* scores, int32_t R, int32_t n, const cq_calib* calib, float* out,
+                       float* row_minmax, void* stream) {
+  if (R < 0 || n < 1 || (int64_t)R * n >= ((int64_t)1 << 40) || calib == nullptr) return CQ_ERR_INVALID_ARG;
+  if (R > 0 && (scores == nullptr || out == nullptr)) return CQ_ERR_INVALID_ARG;
+  clear_stale_hip_error();
+  return from_hip(cqi::calibrate_rows(scores, R, n, calib->enabled, calib->a_lo, calib->c_lo, calib->a_hi,
+                                      calib->c_hi, out, row_minmax, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
+size_t cq_decode_attn_fp16_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d) {
+  if (!fits(B, Hkv, N, d) || Hkv <= 0 || Hq % Hkv != 0 || N < 1) return 0;
+  return cqi::decode_fp16_ws(B, Hq, Hkv, N, d);
+}
+
+cq_status cq_decode_attn_fp16(const void* q, const void* k, const void* v, int32_t B, int32_t Hq, int32_t Hkv,
+                              int32_t N, int32_t d, float sm_scale, void* out, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  if (!fits(B, Hkv, N, d) || !fits(B, Hq, 1, d) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || N < 1 || d <= 0)
+    return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return CQ_ERR_INVALID_ARG;
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  if (Hq / Hkv > 8) return CQ_ERR_UNSUPPORTED;
+  const size_t need = cqi::decode_fp16_ws(B, Hq, Hkv, N, d);
+  if (B > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
+  clear_stale_hip_error();
+  return from_hip(cqi::decode_fp16(q, k, v, B, Hq, Hkv, N, d, sm_scale, out, workspace, (hipStream_t)stream));
+}
+
+}  // extern "C"

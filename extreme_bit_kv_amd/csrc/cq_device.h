@@ -1,0 +1,75 @@
+// Device-side helpers shared by the libcq kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace cqd {
+
+constexpr int kD = 128;          // head dimension supported by this build
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(__half v) { return __half2float(v); }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+template <> __device__ __forceinline__ __half from_f32<__half>(float v) { return __float2half_rn(v); }
+
+// Bit offset of element e inside a packed 32-bit word (see cq.h).
+__host__ __device__ __forceinline__ int code_off(int e, int bits) {
+  return 8 * (e & 3) + bits * (e >> 2);
+}
+
+// Error-free sum: a + b == s + e exactly (round-to-nearest, no reassociation).
+__device__ __forceinline__ void two_sum(double a, double b, double& s, double& e) {
+  s = a + b;
+  double bb = s - a;
+  e = (a - (s - bb)) + (b - bb);
+}
+
+// Exact sign of a + b + c for finite doubles (Shewchuk's grow-expansion: the
+// result is a non-overlapping expansion whose most significant non-zero
+// component carries the sign of the exact sum).
+__device__ __forceinline__ int exact_sign3(double a, double b, double c) {
+  double q, h0;
+  two_sum(b, a, q, h0);            // a + b = q + h0
+  double g0, g1, q2, q3;
+  two_sum(c, h0, q2, g0);          // grow by c
+  two_sum(q2, q, q3, g1);
+  double top = q3 != 0.0 ? q3 : (g1 != 0.0 ? g1 : g0);
+  return (top > 0.0) - (top < 0.0);
+}
+
+// Round-half-to-even code of (x - mn) * L / (mx - mn), decided exactly.
+// `t` is an estimate of that quotient whose absolute error is far below
+// 2^-8; when it is not close to a half-integer the nearest integer is already
+// certain, otherwise the half-integer threshold k + 1/2 is tested exactly via
+// sign(2L*x - (2k+1)*mx + (2k+1-2L)*mn); each product is exact in float64
+// because x, mn, mx are float32-representable and the factors are < 2^10.
+__device__ __forceinline__ int exact_code(float x, float mn, float mx, double t, int L) {
+  double fl = floor(t);
+  double fr = t - fl;
+  int c;
+  if (fabs(fr - 0.5) > 0.0078125) {
+    c = (int)rint(t);
+  } else {
+    int k = (int)fl;
+    k = k < 0 ? 0 : (k > L - 1 ? L - 1 : k);
+    int s = exact_sign3(2.0 * L * (double)x, -(double)(2 * k + 1) * (double)mx,
+                        (double)(2 * k + 1 - 2 * L) * (double)mn);
+    c = k + ((s > 0) || (s == 0 && (k & 1)));
+  }
+  return c < 0 ? 0 : (c > L ? L : c);
+}
+
+// Order-preserving map float -> int32 (for integer atomics on floats).
+__device__ __forceinline__ int f2ord(float f) {
+  int i = __float_as_int(f);
+  return i >= 0 ? i : (i ^ 0x7FFFFFFF);
+}
+__device__ __forceinline__ float ord2f(int i) {
+  return __int_as_float(i >= 0 ? i : (i ^ 0x7FFFFFFF));
+}
+
+}  // namespace cqd

@@ -1,0 +1,83 @@
+// Internal launch interface between the C-ABI layer (cq_api.cpp) and the
+// kernel translation units.  Host-side only; no HIP kernel code here.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/cq.h"
+
+namespace cqi {
+
+constexpr int kHeadDim = 128;    // head dimension implemented by the kernels
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Launch and return the launch status from the enclosing function on failure.
+#define CQ_LAUNCH(...)                                 \
+  do {                                                 \
+    hipLaunchKernelGGL(__VA_ARGS__);                   \
+    hipError_t cq_launch_err_ = hipGetLastError();     \
+    if (cq_launch_err_ != hipSuccess) return cq_launch_err_; \
+  } while (0)
+
+// ---- quantization -------------------------------------------------------
+struct QuantArgs {
+  const void* x;
+  int dtype;            // cq_dtype
+  int B, H, n, d, bits, layout;
+  uint32_t* codes;
+  float* scale;
+  float* minv;
+  void* ws;
+  hipStream_t stream;
+};
+size_t quant_generic_ws(int B, int H, int n, int d);
+hipError_t quant_generic(const QuantArgs& a);
+
+size_t quant_fused_ws(int B, int H, int n, int d);
+bool quant_fused_supported(const QuantArgs& a);
+hipError_t quant_fused(const QuantArgs& a);
+
+// ---- decode -------------------------------------------------------------
+struct DecodeArgs {
+  const void* q;
+  int q_dtype;
+  const uint32_t* k_codes;
+  const float* k_scale;
+  const float* k_min;
+  const uint32_t* v_codes;
+  const float* v_scale;
+  const float* v_min;
+  const void* k_tail;
+  const void* v_tail;
+  int tail_dtype;
+  int B, Hq, Hkv, n, T, d, bits;
+  float sm_scale;
+  int calib_on;
+  float a_lo, c_lo, a_hi, c_hi;
+  void* out;
+  int out_dtype;
+  void* ws;
+  int splits;           // generic path: 0 = automatic
+  hipStream_t stream;
+};
+int decode_generic_splits(int n, int units, int requested);
+size_t decode_generic_ws(int B, int Hq, int Hkv, int n, int T, int d, int splits);
+hipError_t decode_generic(const DecodeArgs& a);
+
+size_t decode_fast_ws(int B, int Hq, int Hkv, int n, int T, int d);
+bool decode_fast_supported(const DecodeArgs& a);
+hipError_t decode_fast(const DecodeArgs& a);
+
+// ---- calibration --------------------------------------------------------
+hipError_t calibrate_rows(const float* scores, int R, int n, int enabled, float a_lo, float c_lo,
+                          float a_hi, float c_hi, float* out, float* row_minmax, hipStream_t st);
+
+// ---- fp16 baseline ------------------------------------------------------
+size_t decode_fp16_ws(int B, int Hq, int Hkv, int N, int d);
+hipError_t decode_fp16(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N,
+                       int d, float sm_scale, void* out, void* ws, hipStream_t st);
+
+}  // namespace cqi

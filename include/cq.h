@@ -1,0 +1,203 @@
+/*
+ * cq.h — C ABI of libcq, a gfx950 (MI355X) implementation of the CalibQuant
+ * visual-KV decode path: channel-wise b-bit quantization of the visual KV
+ * cache, decode attention that reads only the packed integer codes with the
+ * per-channel scale and minimum folded into the query and the output
+ * ("post-scaling"), and the calibration map g on the pre-softmax scores.
+ *
+ * Sources (cited by page title and section):
+ *   [ART] QbitAI article on CalibQuant, "在 InternVL-2.5 上达成 10 倍吞吐量提升",
+ *         section "Method": part 1 channel-wise KV-cache quantization,
+ *         part 2 post-scaling KV-cache management, part 3 post-quantization
+ *         calibration.
+ *   [ABS] "CalibQuant: 1-Bit KV Cache Quantization for Multimodal LLMs",
+ *         abstract (papers.pytorch.kr): plug-and-play, visual-cache
+ *         quantization, 1-bit, Triton runtime.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device buffers are device pointers (hipMalloc'd or
+ *     torch CUDA tensors), caller-allocated and caller-owned; all tensors are
+ *     contiguous, row-major, in the shapes given.  `calib` and `opts` are host
+ *     pointers.  The library never allocates or frees device memory and keeps
+ *     no state between calls.
+ *   - `stream` is a hipStream_t (NULL = the default stream).  Every call only
+ *     enqueues work on it and returns; results are visible after the stream
+ *     is synchronized.  Calls that share a workspace must not overlap.
+ *   - Arguments are validated before anything is enqueued.  On a non-CQ_OK
+ *     status nothing has been enqueued and no output byte has been written.
+ *     CQ_ERR_HIP means a HIP launch call failed (work enqueued before the
+ *     failing launch may still run).  Faults inside kernels surface at the
+ *     caller's next synchronization, as for any HIP kernel.
+ *   - No C++ exception crosses the ABI.
+ *
+ * Packed code format (this library's storage format; the pages only say that
+ * the cache keeps b-bit integer codes plus a per-channel scale and bias):
+ *   b in {1,2,4,8}; L = 2^b - 1; E = 32/b codes per 32-bit word.  Element e
+ *   (0 <= e < E) of a word occupies bits [off(e), off(e)+b) with
+ *        off(e) = 8*(e mod 4) + b*floor(e/4),
+ *   so (word >> (b*s)) & (L*0x01010101) yields elements 4s..4s+3 in bytes 0..3.
+ *   CQ_LAYOUT_K  codes[B][H][W][n], W = d*b/32: word (b,h,w,i) holds channels
+ *                w*E .. w*E+E-1 of token i.
+ *   CQ_LAYOUT_V  codes[B][H][R][d], R = ceil(n/E): word (b,h,r,j) holds tokens
+ *                r*E .. r*E+E-1 of channel j; bits of tokens >= n are 0.
+ *   K is contracted over channels and V over tokens, so each layout keeps the
+ *   contraction index inside a word.
+ */
+#ifndef CQ_H
+#define CQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define CQ_ABI_VERSION 1
+
+typedef enum {
+  CQ_OK = 0,
+  CQ_ERR_INVALID_ARG = 1,   /* NULL pointer, negative or inconsistent size, bad enum */
+  CQ_ERR_UNSUPPORTED = 2,   /* valid arguments this build does not implement (e.g. d != 128) */
+  CQ_ERR_WORKSPACE = 3,     /* workspace pointer NULL or smaller than the query returned */
+  CQ_ERR_HIP = 4            /* a HIP runtime call failed */
+} cq_status;
+
+typedef enum { CQ_F16 = 0, CQ_F32 = 1 } cq_dtype;
+
+typedef enum { CQ_LAYOUT_K = 0, CQ_LAYOUT_V = 1 } cq_layout;
+
+/* Calibration map g ([ART] Method part 3).  For each query head the visual
+ * pre-softmax scores s_i (already multiplied by sm_scale) span [m, M]; g is
+ * the affine map sending [m, M] onto [t_lo, t_hi] with
+ *     t_lo = a_lo*m + c_lo,   t_hi = a_hi*M + c_hi,
+ * i.e. g(s) = t_lo + (s - m)*(t_hi - t_lo)/(M - m), and g(s) = t_lo if M == m.
+ * The pages lost g's formula and parameters; this endpoint form covers both a
+ * relative target (a = tau, c = 0) and a fixed one (a = 0).  Text-tail scores
+ * are not calibrated.  enabled == 0 means g is the identity. */
+typedef struct {
+  int32_t enabled;
+  float a_lo, c_lo;
+  float a_hi, c_hi;
+} cq_calib;
+
+/* Execution path selection, for tests and tuning (NULL opts = automatic). */
+typedef enum { CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2 } cq_path;
+typedef struct {
+  int32_t path;     /* cq_path; CQ_PATH_FAST on an unsupported shape -> CQ_ERR_UNSUPPORTED */
+  int32_t splits;   /* generic decode: token splits per (batch, kv head); 0 = automatic;
+                       clamped to [1, min(64, ceil(n/32))] */
+} cq_opts;
+
+/* ABI version of the loaded library (CQ_ABI_VERSION). */
+int32_t cq_abi_version(void);
+
+/* hipError_t of the most recent CQ_ERR_HIP returned on the calling thread
+ * (0 if none).  A HIP error left pending by earlier calls of other code on the
+ * thread is cleared, not reported, when an entry point starts its launches. */
+int32_t cq_last_hip_error(void);
+
+/* Human-readable name of a status code; never NULL. */
+const char* cq_status_str(cq_status s);
+
+/* ------------------------------------------------------------------------
+ * cq_quantize_kv — channel-wise b-bit quantization and bit-packing of one
+ * K or V cache tensor ([ART] Method part 1: uniform integer quantization with
+ * the range refined per channel over the n tokens of one head; the same is
+ * applied to V).
+ *
+ *   x         device, [B][H][n][d] of x_dtype (CQ_F16 or CQ_F32), finite values
+ *   bits      1, 2, 4 or 8
+ *   layout    CQ_LAYOUT_K or CQ_LAYOUT_V (see the packed format above)
+ *   codes     device, uint32 words in `layout` for every (b, h)
+ *   scale     device, float32 [B][H][d]: (max - min)/L, correctly rounded
+ *   minv      device, float32 [B][H][d]: per-channel minimum (exact)
+ *   workspace device, >= cq_quantize_kv_workspace(...) bytes (may be NULL
+ *             when that is 0)
+ *
+ * For each (b, h, channel j) with mn = min_i x, mx = max_i x over the n tokens:
+ *   code(i, j) = round-half-to-even((x_ij - mn)*L/(mx - mn)), decided exactly;
+ *   code = 0 for every token of a channel with mx == mn (scale is then 0).
+ * n == 0 writes scale = minv = 0 and no code word.  Requires d*b % 32 == 0.
+ * ------------------------------------------------------------------------ */
+size_t cq_quantize_kv_workspace(int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits);
+
+cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype,
+                         int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits,
+                         cq_layout layout,
+                         uint32_t* codes, float* scale, float* minv,
+                         void* workspace, size_t workspace_bytes,
+                         const cq_opts* opts, void* stream);
+
+/* ------------------------------------------------------------------------
+ * cq_decode_attn — one decode step of attention over a quantized visual
+ * cache plus a full-precision text tail ([ART] Method parts 2 and 3; only
+ * the visual cache is quantized, [ABS]).
+ *
+ *   q          device, [B][Hq][d] of q_dtype; query head hq reads kv head
+ *              hq / (Hq/Hkv)
+ *   k_codes    device, CQ_LAYOUT_K words of the visual keys   [B][Hkv][..]
+ *   k_scale, k_min  device, float32 [B][Hkv][d]
+ *   v_codes    device, CQ_LAYOUT_V words of the visual values [B][Hkv][..]
+ *   v_scale, v_min  device, float32 [B][Hkv][d]
+ *   k_tail, v_tail  device, [B][Hkv][T][d] of tail_dtype; NULL iff T == 0
+ *   sm_scale   softmax scale applied to q.k (e.g. 1/sqrt(d))
+ *   calib      host pointer or NULL (= calibration off)
+ *   out        device, [B][Hq][d] of out_dtype
+ *
+ * Computes, per query head, with s_i = sm_scale*(q*k_scale).c_i + sm_scale*q.k_min
+ * for visual token i (the post-scaled form of sm_scale*q.k_hat_i),
+ * s^t_j = sm_scale*q.kt_j for tail token j, and p = softmax([g(s), s^t]):
+ *   out = v_scale * (sum_i p_i c^V_i) + (sum_i p_i)*v_min + sum_j p^t_j vt_j.
+ * Accumulation is float32.  Requires n + T >= 1, Hq % Hkv == 0, d == 128.
+ * ------------------------------------------------------------------------ */
+size_t cq_decode_attn_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n,
+                                int32_t T, int32_t d, int32_t bits);
+
+cq_status cq_decode_attn(const void* q, cq_dtype q_dtype,
+                         const uint32_t* k_codes, const float* k_scale, const float* k_min,
+                         const uint32_t* v_codes, const float* v_scale, const float* v_min,
+                         const void* k_tail, const void* v_tail, cq_dtype tail_dtype,
+                         int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t T,
+                         int32_t d, int32_t bits, float sm_scale,
+                         const cq_calib* calib,
+                         void* out, cq_dtype out_dtype,
+                         void* workspace, size_t workspace_bytes,
+                         const cq_opts* opts, void* stream);
+
+/* ------------------------------------------------------------------------
+ * cq_calibrate — the calibration map g on its own ([ART] Method part 3):
+ * for every row r of scores[R][n], m = min, M = max, and
+ * out[r][i] = g(scores[r][i]) as defined for cq_calib (computed in float64,
+ * rounded to float32).  calib->enabled == 0 copies the scores.
+ *
+ *   scores      device, float32 [R][n]
+ *   out         device, float32 [R][n]; may alias scores
+ *   row_minmax  device, float32 [R][2] receiving (m, M), or NULL
+ * Requires n >= 1.
+ * ------------------------------------------------------------------------ */
+cq_status cq_calibrate(const float* scores, int32_t R, int32_t n,
+                       const cq_calib* calib, float* out, float* row_minmax,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * cq_decode_attn_fp16 — comparison baseline, not part of the method:
+ * unquantized softmax decode attention over N fp16 tokens
+ * (out = softmax(sm_scale * q.K^T) V per query head, float32 accumulation).
+ *
+ *   q    device, fp16 [B][Hq][d];   k, v  device, fp16 [B][Hkv][N][d]
+ *   out  device, fp16 [B][Hq][d];   workspace >= cq_decode_attn_fp16_workspace
+ * Requires N >= 1, Hq % Hkv == 0, d == 128.
+ * ------------------------------------------------------------------------ */
+size_t cq_decode_attn_fp16_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d);
+
+cq_status cq_decode_attn_fp16(const void* q, const void* k, const void* v,
+                              int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                              float sm_scale, void* out,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CQ_H */

@@ -1,0 +1,115 @@
+"""The C-ABI library loads, exports every entry point include/cq.h declares,
+and rejects invalid arguments before touching the GPU (no GPU needed: only
+validation paths are exercised, and they return before any HIP call)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+cqb = pytest.importorskip("extreme_bit_kv_amd", reason="libcq.so not built")
+lib = cqb.lib
+
+FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+
+
+def _declared():
+    text = open(os.path.join(ROOT, "include", "cq.h")).read()
+    return sorted(set(re.findall(r"^\s*(?:[\w\*]+\s+)+\**(cq_\w+)\s*\(", text, re.M)))
+
+
+def test_header_and_exports_agree():
+    decl = _declared()
+    assert decl and set(decl) == set(cqb.EXPORTED)
+    for name in decl:
+        assert hasattr(lib, name), name
+
+
+def test_version_and_status_strings():
+    assert lib.cq_abi_version() == 1
+    for s in range(5):
+        assert lib.cq_status_str(s)
+    assert b"unknown" in lib.cq_status_str(99)
+
+
+def test_workspace_queries():
+    assert lib.cq_quantize_kv_workspace(64, 8, 8192, 128, 1) > 0
+    assert lib.cq_quantize_kv_workspace(1, 1, 256, 128, 3) == 0          # bad bits
+    assert lib.cq_decode_attn_workspace(16, 32, 8, 3328, 64, 128, 1) > 0
+    assert lib.cq_decode_attn_workspace(16, 30, 8, 3328, 64, 128, 1) == 0  # Hq % Hkv
+    assert lib.cq_decode_attn_fp16_workspace(4, 32, 8, 3392, 128) > 0
+    assert lib.cq_decode_attn_fp16_workspace(4, 32, 8, 0, 128) == 0
+
+
+def _quant(**kw):
+    a = dict(x=FAKE, dt=cqb.CQ_F16, B=1, H=1, n=64, d=128, bits=1, layout=cqb.CQ_LAYOUT_K, codes=FAKE,
+             scale=FAKE, minv=FAKE, ws=FAKE, wsb=1 << 30, opts=None)
+    a.update(kw)
+    return lib.cq_quantize_kv(a["x"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["bits"], a["layout"],
+                              a["codes"], a["scale"], a["minv"], a["ws"], a["wsb"], a["opts"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(scale=None), 1), (dict(minv=None), 1),
+    (dict(bits=3), 1), (dict(bits=0), 1), (dict(dt=7), 1), (dict(layout=2), 1), (dict(n=-1), 1),
+    (dict(B=-1), 1), (dict(d=48, bits=1), 1), (dict(d=64), 2), (dict(d=256), 2),
+    (dict(ws=None), 3), (dict(wsb=16), 3),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(9, 0))), 1),
+])
+def test_quantize_rejects(kw, status):
+    assert _quant(**kw) == status
+
+
+def _decode(**kw):
+    a = dict(q=FAKE, qdt=0, kc=FAKE, ks=FAKE, km=FAKE, vc=FAKE, vs=FAKE, vm=FAKE, kt=FAKE, vt=FAKE, tdt=0,
+             B=2, Hq=32, Hkv=8, n=64, T=8, d=128, bits=1, sm=0.088, calib=None, out=FAKE, odt=0,
+             ws=FAKE, wsb=1 << 30, opts=None)
+    a.update(kw)
+    return lib.cq_decode_attn(a["q"], a["qdt"], a["kc"], a["ks"], a["km"], a["vc"], a["vs"], a["vm"], a["kt"],
+                              a["vt"], a["tdt"], a["B"], a["Hq"], a["Hkv"], a["n"], a["T"], a["d"], a["bits"],
+                              a["sm"], a["calib"], a["out"], a["odt"], a["ws"], a["wsb"], a["opts"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(kc=None), 1), (dict(vs=None), 1), (dict(kt=None), 1),
+    (dict(T=0), 1),                                   # tails given but T == 0
+    (dict(n=0, T=0, kt=None, vt=None), 1),            # nothing to attend over
+    (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(bits=5), 1), (dict(qdt=3), 1), (dict(odt=3), 1),
+    (dict(tdt=2), 1), (dict(sm=float("nan")), 1), (dict(d=64), 2), (dict(Hq=80, Hkv=8), 2),
+    (dict(ws=None), 3), (dict(wsb=8), 3),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
+])
+def test_decode_rejects(kw, status):
+    assert _decode(**kw) == status
+
+
+def test_calibrate_rejects():
+    c = cqb.cq_calib(1, 0.9, 0.0, 0.8, 0.0)
+    assert lib.cq_calibrate(FAKE, 4, 0, ctypes.byref(c), FAKE, None, None) == 1
+    assert lib.cq_calibrate(None, 4, 8, ctypes.byref(c), FAKE, None, None) == 1
+    assert lib.cq_calibrate(FAKE, 4, 8, None, FAKE, None, None) == 1
+    assert lib.cq_calibrate(FAKE, -1, 8, ctypes.byref(c), FAKE, None, None) == 1
+
+
+def test_fp16_baseline_rejects():
+    f = lib.cq_decode_attn_fp16
+    assert f(None, FAKE, FAKE, 1, 32, 8, 64, 128, 0.1, FAKE, FAKE, 1 << 30, None) == 1
+    assert f(FAKE, FAKE, FAKE, 1, 32, 8, 0, 128, 0.1, FAKE, FAKE, 1 << 30, None) == 1
+    assert f(FAKE, FAKE, FAKE, 1, 32, 8, 64, 64, 0.1, FAKE, FAKE, 1 << 30, None) == 2
+    assert f(FAKE, FAKE, FAKE, 1, 32, 8, 64, 128, 0.1, FAKE, None, 0, None) == 3
+
+
+def test_empty_batch_is_a_no_op_without_gpu_work():
+    # B == 0: valid, nothing to do, no pointer needed
+    assert _quant(B=0, x=None, codes=None, scale=None, minv=None, ws=None, wsb=0) == 0
+    assert _decode(B=0, q=None, out=None, kc=None, ks=None, km=None, vc=None, vs=None, vm=None, kt=None,
+                   vt=None, ws=None, wsb=0) == 0
+
+
+def test_binding_has_no_cpu_fallback():
+    src = open(os.path.join(ROOT, "extreme_bit_kv_amd", "_binding.py")).read()
+    assert "import oracle" not in src and "from oracle" not in src
+    for f in os.listdir(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc")):
+        assert "oracle" not in open(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc", f)).read()
