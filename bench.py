@@ -1,0 +1,393 @@
+"""Throughput of the CalibQuant visual-KV path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_n8192]
+
+One step is one pass of the whole path over one batch of the workload: the
+prefill quantization of the full visual K and V caches (cq_quantize_kv, twice)
+followed by one calibrated decode-attention step for every sequence
+(cq_decode_attn).  Inputs are seeded synthetic tensors already resident in HBM
+when timing starts.  W untimed steps run first, then exactly K steps are timed
+with the device synchronized on both sides; HIP events on the launch stream
+time every call.  One JSON line is printed.
+
+Beside the step it reports the decode alone with the Infinity Cache flushed
+before each call, the float16 unquantized decode baseline over the same
+tokens, the roofline of each kernel, and the CPU oracle timed on a bounded
+sample of the same workload (the ``cpu_baseline`` leg; the only place this
+file touches the oracle).
+
+Profiling helpers (used to produce profiles/):
+    --only {step,copy}     run only the timed steps, or only a 1 GiB copy
+                           kernel (the HBM-counter calibration reference)
+    --summarize DIR ...    turn rocprofv3 CSV output dirs into profiles/ files
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E peak, GB/s
+METRIC = "1-bit KV decode-attn seq-steps/s + % HBM peak, n=8192, GQA 32q/8kv d=128"
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+# ---------------------------------------------------------------------------
+# algorithmic byte counts
+# ---------------------------------------------------------------------------
+
+def quant_bytes(cfg):
+    """One cq_quantize_kv launch over one of K or V: read fp16 x, write codes and 2 fp32 vectors."""
+    units = cfg.B * cfg.Hkv
+    elem = 2 if cfg.dtype == "float16" else 4
+    return units * (cfg.n * cfg.d * elem + cfg.n * cfg.d * cfg.bits // 8 + 2 * cfg.d * 4)
+
+
+def decode_bytes(cfg):
+    """One cq_decode_attn launch: K and V codes, fp16 tails, 4 fp32 parameter vectors, q and out."""
+    units = cfg.B * cfg.Hkv
+    G = cfg.Hq // cfg.Hkv
+    per = 2 * cfg.n * cfg.d * cfg.bits // 8 + 2 * cfg.T * cfg.d * 2 + 4 * cfg.d * 4 + 2 * G * cfg.d * 2
+    return units * per
+
+
+def fp16_bytes(cfg):
+    units = cfg.B * cfg.Hkv
+    G = cfg.Hq // cfg.Hkv
+    return units * (2 * (cfg.n + cfg.T) * cfg.d * 2 + 2 * G * cfg.d * 2)
+
+
+def source_digest(*names):
+    h = hashlib.sha256()
+    for name in names:
+        h.update(open(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc", name), "rb").read())
+    return h.hexdigest()[:16]
+
+
+KERNEL_SOURCES = {
+    "quantize": ("quantize_fused.hip", "quantize_generic.hip", "cq_device.h"),
+    "decode": ("decode_fast.hip", "decode_generic.hip", "cq_device.h"),
+}
+
+
+def measured_traffic(workload, op):
+    """HBM bytes per launch from committed rocprofv3 counter runs, or None when
+    missing or taken from different kernel sources."""
+    path = os.path.join(PROFILES, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get(op)
+    if not rec or rec.get("source_digest") != source_digest(*KERNEL_SOURCES[op]):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle leg
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(cfg, K, V, q, kt, vt, sm, calib, budget_s):
+    """Time the oracle (as it stands) on whole (batch, kv head) units of the
+    same workload until ~budget_s seconds of CPU work; one sequence-step is
+    Hkv units."""
+    import numpy as np
+    import oracle
+    from threadpoolctl import threadpool_limits
+    G = cfg.Hq // cfg.Hkv
+    c32 = oracle.Calib(*(float(np.float32(v)) for v in calib)) if calib else None
+    units, t_used = 0, 0.0
+    order = [(b, h) for b in range(cfg.B) for h in range(cfg.Hkv)]
+    rng = np.random.default_rng(0)
+    rng.shuffle(order)
+    for b, h in order:
+        Ku, Vu = K[b, h].cpu().numpy(), V[b, h].cpu().numpy()
+        limiter = threadpool_limits(limits=1)
+        qu = q[b, h * G:(h + 1) * G].cpu().numpy()
+        ktu = kt[b, h].cpu().numpy() if kt is not None else None
+        vtu = vt[b, h].cpu().numpy() if vt is not None else None
+        t0 = time.perf_counter()
+        kc, ks, km, _ = oracle.quantize_unit(Ku, cfg.bits)
+        vc, vs, vm, _ = oracle.quantize_unit(Vu, cfg.bits)
+        oracle.pack(kc, cfg.bits, "K")
+        oracle.pack(vc, cfg.bits, "V")
+        oracle.decode_unit(qu, kc, ks, km, vc, vs, vm, ktu, vtu, sm, c32)
+        t_used += time.perf_counter() - t0
+        limiter.restore_original_limits()
+        units += 1
+        if t_used >= budget_s:
+            break
+    seq_steps = units / cfg.Hkv
+    return {"value": seq_steps / t_used, "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{units} (batch, kv-head) units of {cfg.name} (n={cfg.n}, d={cfg.d}, fp16): quantize + pack "
+                      f"K and V and one {G}-head calibrated decode each, {t_used:.1f} s single-threaded; "
+                      f"{cfg.Hkv} units = 1 sequence-step"}
+
+
+# ---------------------------------------------------------------------------
+# GPU measurement
+# ---------------------------------------------------------------------------
+
+def run(args):
+    import numpy as np
+    import torch
+
+    import extreme_bit_kv_amd as cqb
+    from workloads import (CONFIGS, ROLE_K, ROLE_KTAIL, ROLE_V, ROLE_VTAIL, kv_torch, q_torch)
+
+    cfg = CONFIGS[args.workload]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    print(f"[bench] workload {cfg.name}: B={cfg.B} Hq={cfg.Hq} Hkv={cfg.Hkv} n={cfg.n} T={cfg.T} "
+          f"bits={cfg.bits}", file=sys.stderr, flush=True)
+
+    if args.only == "copy":
+        src = torch.empty(1 << 29, dtype=torch.float16, device=dev).normal_()
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": src.numel() * 2, "copy_bytes_written": dst.numel() * 2,
+                          "launches": 3}))
+        return
+
+    K = kv_torch(cfg.seed, 0, ROLE_K, cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.dtype, dev)
+    V = kv_torch(cfg.seed, 0, ROLE_V, cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.dtype, dev)
+    kt = kv_torch(cfg.seed, 0, ROLE_KTAIL, cfg.B, cfg.Hkv, cfg.T, cfg.d, cfg.dtype, dev) if cfg.T else None
+    vt = kv_torch(cfg.seed, 0, ROLE_VTAIL, cfg.B, cfg.Hkv, cfg.T, cfg.d, cfg.dtype, dev) if cfg.T else None
+    q = q_torch(cfg.seed, 0, cfg.B, cfg.Hq, cfg.d, cfg.dtype, dev)
+    sm = 1.0 / float(np.sqrt(cfg.d))
+    calib = cfg.calib
+
+    # preallocated outputs and workspaces: the timed loop allocates nothing
+    kc, ks, km = cqb.cq_quantize_kv(K, cfg.bits, cqb.CQ_LAYOUT_K)
+    vc, vs, vm = cqb.cq_quantize_kv(V, cfg.bits, cqb.CQ_LAYOUT_V)
+    qws = torch.empty(max(1, cqb.lib.cq_quantize_kv_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
+                      dtype=torch.uint8, device=dev)
+    dws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d,
+                                                              cfg.bits)), dtype=torch.uint8, device=dev)
+    out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float16, device=dev)
+
+    def quant_k():
+        cqb.cq_quantize_kv(K, cfg.bits, cqb.CQ_LAYOUT_K, codes=kc, scale=ks, minv=km, workspace=qws)
+
+    def quant_v():
+        cqb.cq_quantize_kv(V, cfg.bits, cqb.CQ_LAYOUT_V, codes=vc, scale=vs, minv=vm, workspace=qws)
+
+    def decode():
+        cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=cfg.bits, sm_scale=sm,
+                           calib=calib, out=out, workspace=dws)
+
+    for _ in range(args.warmup):
+        quant_k(); quant_v(); decode()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record(stream)
+        quant_k()
+        ev[k][1].record(stream)
+        quant_v()
+        ev[k][2].record(stream)
+        decode()
+        ev[k][3].record(stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    tq_k = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    tq_v = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    td = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
+    if args.only == "step":
+        print(json.dumps({"workload": cfg.name, "steps": args.steps, "ms_per_step": wall * 1e3 / args.steps,
+                          "per_call_ms": {"quantize_k": tq_k * 1e3, "quantize_v": tq_v * 1e3,
+                                          "decode_in_step": td * 1e3}}), flush=True)
+        return
+
+    # decode alone with the Infinity Cache flushed before every call
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for _ in range(max(10, args.steps)):
+        scratch.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        decode()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    td_cold = np.median([a.elapsed_time(b) for a, b in cold]) * 1e-3
+
+    # float16 unquantized baseline over the same n + T tokens, same flush
+    Kf = torch.cat([K, kt], dim=2) if kt is not None else K
+    Vf = torch.cat([V, vt], dim=2) if vt is not None else V
+    of = torch.empty_like(out)
+    fws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n + cfg.T, cfg.d)),
+                      dtype=torch.uint8, device=dev)
+    fcold = []
+    for _ in range(max(10, args.steps)):
+        scratch.zero_()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=of, workspace=fws)
+        b.record(stream)
+        fcold.append((a, b))
+    torch.cuda.synchronize()
+    tf16 = np.median([a.elapsed_time(b) for a, b in fcold]) * 1e-3
+    del Kf, Vf
+
+    qb, db, fb = quant_bytes(cfg), decode_bytes(cfg), fp16_bytes(cfg)
+    tq = 0.5 * (tq_k + tq_v)
+
+    def roof(nbytes, secs, op):
+        ach = nbytes / secs / 1e9
+        traffic = measured_traffic(cfg.name, op)
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    dominant = "quantize" if 2 * tq >= td else "decode"
+    line = {
+        "metric": METRIC,
+        "value": round(cfg.B * args.steps / wall, 1),
+        "unit": "seq-steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3 / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp16 in; 1-bit codes; int/f32 accumulate",
+        "data": "synthetic (seeded outlier-channel K/V, N(0,1) q)",
+        "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "n": cfg.n, "T": cfg.T,
+                   "d": cfg.d, "bits": cfg.bits, "calib": list(calib) if calib else None,
+                   "step": "quantize K + quantize V (full prefill cache) + 1 decode step"},
+        "roofline": roof(qb if dominant == "quantize" else db, tq if dominant == "quantize" else td, dominant),
+        "dominant_kernel": "cq_quantize_kv" if dominant == "quantize" else "cq_decode_attn",
+        "per_call_ms": {"quantize_k": round(tq_k * 1e3, 4), "quantize_v": round(tq_v * 1e3, 4),
+                        "decode_in_step": round(td * 1e3, 4), "decode_cold": round(td_cold * 1e3, 4)},
+        "decode": {"seq_steps_per_s_cold": round(cfg.B / td_cold, 1),
+                   "roofline_cold": roof(db, td_cold, "decode"),
+                   "roofline_in_step": roof(db, td, "decode")},
+        "quantize": {"roofline": roof(qb, tq, "quantize")},
+        "fp16_baseline": {"kernel": "cq_decode_attn_fp16", "ms_cold": round(tf16 * 1e3, 4),
+                          "seq_steps_per_s": round(cfg.B / tf16, 1),
+                          "achieved_GBs": round(fb / tf16 / 1e9, 1),
+                          "speedup_1bit_decode_vs_fp16": round(tf16 / td_cold, 2)},
+        "bytes": {"quantize_per_launch": qb, "decode_per_launch": db, "fp16_decode_per_launch": fb},
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle", file=sys.stderr, flush=True)
+        line["cpu_baseline"] = cpu_baseline(cfg, K, V, q, kt, vt, sm, calib, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries -> profiles/
+# ---------------------------------------------------------------------------
+
+def _rows(pattern):
+    rows = []
+    for f in glob.glob(pattern, recursive=True):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def summarize(dirs, workload, command_note):
+    """Write profiles/<kernel>_<workload>.md from kernel-trace stats and
+    counter CSVs, and profiles/traffic_<workload>.json with HBM bytes per launch
+    scaled by the copy-kernel reference."""
+    os.makedirs(PROFILES, exist_ok=True)
+    stats = []
+    for d in dirs:
+        stats += _rows(os.path.join(d, "**", "*kernel_stats.csv"))
+    counters = []
+    for d in dirs:
+        counters += _rows(os.path.join(d, "**", "*counter_collection.csv"))
+    lines = [f"# rocprofv3 summary — {workload}", "", "Commands:", "", "```", command_note.strip(), "```", ""]
+    if stats:
+        lines += ["## Kernel stats (--kernel-trace --stats)", "",
+                  "| kernel | calls | avg (us) | total (ms) | % |", "|---|---|---|---|---|"]
+        for r in sorted(stats, key=lambda r: -float(r.get("TotalDurationNs", 0))):
+            lines.append(f"| {r['Name'][:90]} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                         f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r.get('Percentage', 0)):.1f} |")
+        lines.append("")
+    traffic = {}
+    if counters:
+        per = {}
+        for r in counters:
+            name = r.get("Kernel_Name", r.get("Kernel-Name", ""))
+            cname = r.get("Counter_Name", r.get("Counter-Name", ""))
+            val = float(r.get("Counter_Value", r.get("Counter-Value", 0)))
+            per.setdefault((name, cname), []).append(val)
+        lines += ["## HBM counters (--pmc, KiB per dispatch, averaged)", "",
+                  "| kernel | counter | dispatches | avg KiB |", "|---|---|---|---|"]
+        for (name, cname), vals in sorted(per.items()):
+            lines.append(f"| {name[:80]} | {cname} | {len(vals)} | {sum(vals) / len(vals):.1f} |")
+        lines.append("")
+        copy_read = [v for (n_, c), vs in per.items() if "neg" in n_.lower() and c == "FETCH_SIZE" for v in vs]
+        copy_write = [v for (n_, c), vs in per.items() if "neg" in n_.lower() and c == "WRITE_SIZE" for v in vs]
+        ref_bytes = (1 << 29) * 2
+        f_read = (sum(copy_read) / len(copy_read) * 1024 / ref_bytes) if copy_read else None
+        f_write = (sum(copy_write) / len(copy_write) * 1024 / ref_bytes) if copy_write else None
+        lines += [f"Copy-kernel reference (1 GiB read + 1 GiB written): FETCH_SIZE factor "
+                  f"{f_read}, WRITE_SIZE factor {f_write} (counter KiB x 1024 / true bytes).", ""]
+
+        def op_bytes(match):
+            tot = 0.0
+            for cname, fac in (("FETCH_SIZE", f_read), ("WRITE_SIZE", f_write)):
+                vals = [v for (n_, c), vs in per.items() if c == cname and any(m in n_ for m in match)
+                        for v in vs]
+                if not vals or not fac:
+                    return None
+                tot += sum(vals) / len(vals) * 1024 / fac
+            return tot
+        for op, match in (("quantize", ("qz_", "qf_")), ("decode", ("dg_", "df_"))):
+            b = op_bytes(match)
+            if b is not None:
+                traffic[op] = {"bytes_per_launch": round(b), "source_digest": source_digest(*KERNEL_SOURCES[op])}
+    name = "summary" if not stats else "kernels"
+    with open(os.path.join(PROFILES, f"{name}_{workload}.md"), "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+    if traffic:
+        with open(os.path.join(PROFILES, f"traffic_{workload}.json"), "w") as fh:
+            json.dump(traffic, fh, indent=1)
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="long_n8192")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--only", choices=["step", "copy"], default=None)
+    ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
+    ap.add_argument("--command-note", default="")
+    args = ap.parse_args()
+    if args.summarize:
+        summarize(args.summarize, args.workload, args.command_note)
+        return
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the path shards by batch or kv head with no "
+              "communication, and no multi-GPU figure is produced. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    run(args)
+
+
+if __name__ == "__main__":
+    main()

@@ -83,12 +83,14 @@ def test_group_sizes_and_ragged_lengths(G, n, path):
 
 @pytest.mark.parametrize("splits", [1, 2, 3, 7, 25])
 def test_split_count_does_not_change_the_result(splits):
+    import torch
     K, V, q, kt, vt = draw_inputs(1, 4, 1, 800, 64, seed=5)
     note(f"decode splits={splits}")
-    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_GENERIC, splits)
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_GENERIC, splits, out_dtype=torch.float32)
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
-    base = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_GENERIC, 1)
-    assert np.max(np.abs(got - base)) <= 1e-5 * max(1.0, np.max(np.abs(base)))
+    base = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_GENERIC, 1, out_dtype=torch.float32)
+    diff = float(np.max(np.abs(got - base)))
+    assert diff <= 1e-5 * max(1.0, float(np.max(np.abs(base)))), f"max |diff| {diff:.3e}"
 
 
 @pytest.mark.parametrize("path", PATHS)
