@@ -113,7 +113,11 @@ const char* cq_status_str(cq_status s);
  *   scale     device, float32 [B][H][d]: (max - min)/L, correctly rounded
  *   minv      device, float32 [B][H][d]: per-channel minimum (exact)
  *   workspace device, >= cq_quantize_kv_workspace(...) bytes (may be NULL
- *             when that is 0)
+ *             when that is 0).  After the call completes, its first int32 is
+ *             a status word: 0, or 1 if a workgroup of the fused path gave up
+ *             waiting for the other chunks of its (batch, head) (the outputs
+ *             are then invalid; this does not happen when the launch is
+ *             co-resident, which the library arranges).
  *
  * For each (b, h, channel j) with mn = min_i x, mx = max_i x over the n tokens:
  *   code(i, j) = round-half-to-even((x_ij - mn)*L/(mx - mn)), decided exactly;

@@ -9,15 +9,29 @@ from helpers import draw_inputs, note, words_u32
 pytestmark = pytest.mark.gpu
 
 cqb = pytest.importorskip("extreme_bit_kv_amd")
-PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO]
+PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST]
 LAYOUTS = {cqb.CQ_LAYOUT_K: "K", cqb.CQ_LAYOUT_V: "V"}
+
+
+def _fast_ok(x_dev, bits):
+    import torch
+    return x_dev.dtype == torch.float16 and bits == 1 and x_dev.shape[2] >= 1
 
 
 def _check_units(x_dev, bits, layout, path, units=None):
     import torch
+    B, H, n, d = x_dev.shape
     note(f"quantize shape={tuple(x_dev.shape)} dtype={x_dev.dtype} bits={bits} layout={LAYOUTS[layout]} path={path}")
-    codes, scale, minv = cqb.cq_quantize_kv(x_dev, bits, layout, path=path)
+    if path == cqb.CQ_PATH_FAST and not _fast_ok(x_dev, bits):
+        with pytest.raises(cqb.CQError) as ei:
+            cqb.cq_quantize_kv(x_dev, bits, layout, path=path)
+        assert ei.value.status == 2          # CQ_ERR_UNSUPPORTED, nothing enqueued
+        return
+    ws = torch.full((cqb.lib.cq_quantize_kv_workspace(B, H, n, d, bits),), 7, dtype=torch.uint8, device="cuda")
+    codes, scale, minv = cqb.cq_quantize_kv(x_dev, bits, layout, path=path, workspace=ws)
     torch.cuda.synchronize()
+    if path != cqb.CQ_PATH_GENERIC and _fast_ok(x_dev, bits):
+        assert int(ws[:4].view(torch.int32).item()) == 0, "cooperative wait timed out"
     B, H = x_dev.shape[:2]
     units = units or [(b, h) for b in range(B) for h in range(H)]
     for b, h in units:
@@ -74,7 +88,7 @@ def test_forced_ties_and_degenerate(bits, dtype, path):
         _check_units(xd, bits, layout, path)
 
 
-@pytest.mark.parametrize("path", PATHS)
+@pytest.mark.parametrize("path", PATHS[:2])
 def test_empty_cache(path):
     import torch
     x = torch.empty((2, 3, 0, 128), dtype=torch.float16, device="cuda")
@@ -100,3 +114,18 @@ def test_long_context_sampled_units(path):
     units = [(0, 0), (31, 4), (63, 7)]
     _check_units(K, 1, 0, path, units)
     _check_units(V, 1, 1, path, units)
+
+
+def test_fused_repeated_launches_are_identical():
+    """The fused kernel's rendezvous state is re-initialised by every call."""
+    import torch
+    K, *_ = draw_inputs(8, 32, 8, 1000, 0, seed=13, host=False)
+    note("quantize fused x5")
+    ref = [t.clone() for t in cqb.cq_quantize_kv(K, 1, 0, path=cqb.CQ_PATH_FAST)]
+    ws = torch.empty((cqb.lib.cq_quantize_kv_workspace(8, 8, 1000, 128, 1),), dtype=torch.uint8, device="cuda")
+    for _ in range(5):
+        got = cqb.cq_quantize_kv(K, 1, 0, path=cqb.CQ_PATH_FAST, workspace=ws)
+        torch.cuda.synchronize()
+        assert int(ws[:4].view(torch.int32).item()) == 0
+        for a, b in zip(ref, got):
+            assert torch.equal(a, b)
