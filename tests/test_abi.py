@@ -78,8 +78,11 @@ def _decode(**kw):
     (dict(n=0, T=0, kt=None, vt=None), 1),            # nothing to attend over
     (dict(Hq=30), 1), (dict(Hkv=0), 1), (dict(bits=5), 1), (dict(qdt=3), 1), (dict(odt=3), 1),
     (dict(tdt=2), 1), (dict(sm=float("nan")), 1), (dict(d=64), 2), (dict(Hq=80, Hkv=8), 2),
-    (dict(ws=None), 3), (dict(wsb=8), 3),
+    # the workspace cases force the split-K path, the one that needs a workspace
+    (dict(ws=None, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
+    (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), bits=2), 2),     # matrix-core path is 1-bit only
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status

@@ -14,7 +14,15 @@ SM = 1.0 / np.sqrt(128.0)
 RELATIVE = (0.9, 0.0, 0.8, 0.0)
 ABSOLUTE = (0.0, -4.0, 0.0, 4.0)
 IDENTITY = (1.0, 0.0, 1.0, 0.0)
-PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO]
+PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST]
+
+
+def fast_ok(q, K, kt, bits):
+    """Shapes the matrix-core decode kernel takes (else CQ_ERR_UNSUPPORTED)."""
+    n, G = K.shape[2], q.shape[1] // K.shape[1]
+    T = 0 if kt is None else kt.shape[2]
+    return (bits == 1 and G in (1, 2, 4) and n % 32 == 0 and -(-n // 128) <= 64 and T <= 256
+            and (T == 0 or kt.dtype == q.dtype))
 
 
 def _run(K, V, q, kt, vt, bits, calib, path=cqb.CQ_PATH_AUTO, splits=0, out_dtype=None):
@@ -22,6 +30,12 @@ def _run(K, V, q, kt, vt, bits, calib, path=cqb.CQ_PATH_AUTO, splits=0, out_dtyp
     n = K.shape[2]
     kc, ks, km = cqb.cq_quantize_kv(K, bits, cqb.CQ_LAYOUT_K)
     vc, vs, vm = cqb.cq_quantize_kv(V, bits, cqb.CQ_LAYOUT_V)
+    if path == cqb.CQ_PATH_FAST and not fast_ok(q, K, kt, bits):
+        with pytest.raises(cqb.CQError) as ei:
+            cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=bits, sm_scale=SM, calib=calib,
+                               path=path)
+        assert ei.value.status == 2
+        pytest.skip("shape not taken by the matrix-core kernel (CQ_ERR_UNSUPPORTED checked)")
     out = cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=bits, sm_scale=SM, calib=calib,
                              path=path, splits=splits, out_dtype=out_dtype)
     torch.cuda.synchronize()
@@ -97,6 +111,8 @@ def test_split_count_does_not_change_the_result(splits):
 def test_tail_only(path):
     import torch
     _, _, q, kt, vt = draw_inputs(2, 8, 2, 0, 16, seed=9)
+    if path == cqb.CQ_PATH_FAST:
+        pytest.skip("covered by AUTO (n = 0 takes the matrix-core kernel)")
     z = torch.zeros((2, 2, 128), dtype=torch.float32, device="cuda")
     note(f"decode n=0 T=16 path={path}")
     out = cqb.cq_decode_attn(q, None, z, z, None, z, z, kt, vt, n=0, bits=1, sm_scale=SM, calib=RELATIVE,
@@ -130,7 +146,7 @@ def test_oracle_packed_codes_decode():
     vw, vs, vm, vc = oracle.quantize(V.cpu().numpy(), 1, "V")
     dev = lambda a, dt: torch.from_numpy(np.ascontiguousarray(a)).to("cuda", dt)
     note("decode from oracle-packed codes")
-    for path in PATHS:
+    for path in PATHS[:2]:
         out = cqb.cq_decode_attn(q, dev(kw.view(np.int32), torch.int32), dev(ks, torch.float32),
                                  dev(km, torch.float32), dev(vw.view(np.int32), torch.int32),
                                  dev(vs, torch.float32), dev(vm, torch.float32), kt, vt, n=n, bits=1,
@@ -166,3 +182,13 @@ def test_bit_width_sweep_sampled(bits):
     note(f"decode bit sweep bits={bits}")
     got = _run(K, V, q, kt, vt, bits, None)
     _compare(got, _oracle(K, V, q, kt, vt, bits, None, [(0, 1), (31, 6)]), 4)
+
+
+@pytest.mark.parametrize("n", [32, 96, 128, 2048, 2080, 4096, 4224, 8192])
+@pytest.mark.parametrize("G", [1, 2, 4])
+def test_fast_kernel_tile_counts(n, G):
+    """Every register/LDS split of the matrix-core kernel (1, 2 and 4 tiles per wave), ragged tiles."""
+    K, V, q, kt, vt = draw_inputs(1, 2 * G, 2, n, 64, seed=n + G)
+    note(f"decode fast n={n} G={G}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST)
+    _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), G)
