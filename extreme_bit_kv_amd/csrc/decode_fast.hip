@@ -133,24 +133,34 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   __shared__ float s_psum[kWaves][4];
 
   // ---- prologue: post-scaled query, fixed-point digits -------------------
-  if (tid < 4 * 128) {
+  __shared__ double s_c0p[8];
+  __shared__ float s_mqp[8];
+  if (tid < 4 * 128) {                          // waves 0..7: head = wave / 2
     const int hh = tid >> 7, j = tid & 127;
     float qv = 0.f, qp = 0.f;
+    double pr = 0.0;
     if (hh < G) {
       qv = P.sm * ld_any(P.q, ((size_t)b * P.Hq + h * G + hh) * 128 + j, P.q_f32);
       qp = qv * P.ks[(size_t)unit * 128 + j];
+      pr = (double)qv * (double)P.km[(size_t)unit * 128 + j];
     }
     s_q[hh][j] = qv;
     s_qp[hh][j] = qp;
+    float aq = fabsf(qp);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      pr += __shfl_xor(pr, off);
+      aq = fmaxf(aq, __shfl_xor(aq, off));
+    }
+    if (lane == 0) {
+      s_c0p[wave] = pr;
+      s_mqp[wave] = aq;
+    }
   }
   __syncthreads();
   if (tid < 4) {
-    double c0 = 0.0;
-    float mq = 0.f;
-    for (int j = 0; j < 128; ++j) {
-      c0 += (double)s_q[tid][j] * (double)P.km[(size_t)unit * 128 + j];
-      mq = fmaxf(mq, fabsf(s_qp[tid][j]));
-    }
+    const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
+    const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
     int F = 0;
     if (mq > 0.f) F = 21 - ilogbf(mq);
     s_F[tid] = F;
@@ -263,25 +273,31 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
     s_red[wave][oh][1] = vmax;
   }
   __syncthreads();
-  if (tid < G) {
-    float m = INFINITY, M = -INFINITY;
-    for (int w = 0; w < kWaves; ++w) {
-      m = fminf(m, s_red[w][tid][0]);
-      M = fmaxf(M, s_red[w][tid][1]);
-    }
-    float lam = 1.f, mu = 0.f, vis_max = M;
-    if (P.calib_on && n > 0) {
-      const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
-      lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
-      mu = t_lo - lam * m;
-      vis_max = fmaxf(t_lo, t_hi);
-    }
+  if (wave < G) {                               // wave hh settles head hh
+    const int hh = wave;
+    float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
+    float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
     float tmax = -INFINITY;
-    for (int j = 0; j < T; ++j) tmax = fmaxf(tmax, s_ts[tid][j]);
-    const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
-    s_lam[tid] = lam * kLog2e;                  // p = 2^(s * lam' + mu')
-    s_mu[tid] = (mu - top) * kLog2e;
-    s_tmax[tid] = top;
+    for (int j = lane; j < T; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      m = fminf(m, __shfl_xor(m, off));
+      M = fmaxf(M, __shfl_xor(M, off));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+    }
+    if (lane == 0) {
+      float lam = 1.f, mu = 0.f, vis_max = M;
+      if (P.calib_on && n > 0) {
+        const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
+        lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
+        mu = t_lo - lam * m;
+        vis_max = fmaxf(t_lo, t_hi);
+      }
+      const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
+      s_lam[hh] = lam * kLog2e;                 // p = 2^(s * lam' + mu')
+      s_mu[hh] = (mu - top) * kLog2e;
+      s_tmax[hh] = top;
+    }
   }
   __syncthreads();
   // tail probabilities (in place)
@@ -382,6 +398,33 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
   __syncthreads();
+  // text-tail values: thread (half, head, channel) sums every other tail
+  // token, 16 independent loads in flight
+  __shared__ float s_tail[2][4][128];
+  __shared__ float s_ptail[2][4];
+  {
+    const int half = tid >> 9, hh = (tid >> 7) & 3, j = tid & 127;
+    float tail = 0.f, pt = 0.f;
+    if (hh < G) {
+      for (int t0 = half; t0 < T; t0 += 32) {
+        float vv[16], pp[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int t = t0 + 2 * q;
+          vv[q] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + j, P.tail_f32) : 0.f;
+          pp[q] = t < T ? s_ts[hh][t] : 0.f;
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          pt += pp[q];
+          tail = fmaf(pp[q], vv[q], tail);
+        }
+      }
+    }
+    s_tail[half][hh][j] = tail;
+    if (j == 0) s_ptail[half][hh] = pt;
+  }
+  __syncthreads();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     float sv = 0.f, pv = 0.f;
@@ -390,12 +433,8 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       sv += s_vred[w][hh][j];
       pv += s_psum[w][hh];
     }
-    float tail = 0.f, pt = 0.f;
-    for (int t = 0; t < T; ++t) {
-      const float p = s_ts[hh][t];
-      pt += p;
-      tail = fmaf(p, ld_any(P.vt, ((size_t)unit * T + t) * 128 + j, P.tail_f32), tail);
-    }
+    const float tail = s_tail[0][hh][j] + s_tail[1][hh][j];
+    const float pt = s_ptail[0][hh] + s_ptail[1][hh];
     float o = tail;
     if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
     o /= (pv + pt);
