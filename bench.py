@@ -344,19 +344,21 @@ def summarize(dirs, workload, command_note):
         lines += [f"Copy-kernel reference (1 GiB read + 1 GiB written): FETCH_SIZE factor "
                   f"{f_read}, WRITE_SIZE factor {f_write} (counter KiB x 1024 / true bytes).", ""]
 
-        def op_bytes(match):
+        def op_bytes(kernels):
+            # one call launches each kernel in `kernels` once: sum their per-dispatch averages
             tot = 0.0
             for cname, fac in (("FETCH_SIZE", f_read), ("WRITE_SIZE", f_write)):
-                vals = [v for (n_, c), vs in per.items() if c == cname and any(m in n_ for m in match)
-                        for v in vs]
-                if not vals or not fac:
-                    return None
-                tot += sum(vals) / len(vals) * 1024 / fac
+                for kern in kernels:
+                    vals = [v for (n_, c), vs in per.items() if c == cname and kern in n_ for v in vs]
+                    if not vals or not fac:
+                        return None
+                    tot += sum(vals) / len(vals) * 1024 / fac
             return tot
-        for op, match in (("quantize", ("qz_", "qf_")), ("decode", ("dg_", "df_"))):
-            b = op_bytes(match)
+        for op, kernels in (("quantize", ("qf_init", "qf_b1")), ("decode", ("df_b1",))):
+            b = op_bytes(kernels)
             if b is not None:
-                traffic[op] = {"bytes_per_launch": round(b), "source_digest": source_digest(*KERNEL_SOURCES[op])}
+                traffic[op] = {"bytes_per_launch": round(b), "kernels": list(kernels),
+                               "source_digest": source_digest(*KERNEL_SOURCES[op])}
     name = "summary" if not stats else "kernels"
     with open(os.path.join(PROFILES, f"{name}_{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")

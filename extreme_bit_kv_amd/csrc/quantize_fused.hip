@@ -5,8 +5,8 @@
 // becomes 1 exactly when it lies above the midpoint of its channel's range
 // (round-half-to-even sends the midpoint itself to 0).
 //
-// The input is read from HBM once.  A persistent, cooperatively launched grid
-// walks (unit, chunk) items, a unit being one (batch, head) and a chunk 512
+// The input is read from HBM once.  A persistent grid walks (unit, chunk)
+// items, a unit being one (batch, head) and a chunk 512
 // tokens (128 KB).  A workgroup keeps its chunk in registers, reduces the
 // chunk's per-channel min/max, meets the other chunks of the unit at a
 // rendezvous in the workspace, and then decides the codes from the registers:
@@ -16,9 +16,13 @@
 // values never rounds to zero, and t is never -0).
 //
 // Items are dealt so that all chunks of a unit run in the same round on
-// distinct, co-resident workgroups (the grid is a multiple of the chunk
-// count), so every wait ends.  The waits are also bounded: past the bound the
-// workgroup records a time-out in the workspace status word and goes on.
+// distinct workgroups (the grid is a multiple of the chunk count), and the
+// grid is never larger than the number of workgroups the device holds at
+// once, so on a device not filled by other work every wait ends.  The waits
+// are also bounded: past the bound the workgroup records a time-out in the
+// workspace status word and goes on.  (A cooperative launch would guarantee
+// co-residency formally, but on this runtime it costs about 20 us of
+// serialization around the kernel, some 8% of a long-context launch.)
 //
 // Rendezvous: every chunk publishes, per channel, one 32-bit word holding the
 // float16 bit patterns of its min and max; chunk 0 of the unit (the leader)
@@ -44,7 +48,7 @@ constexpr int kChunk = 4 * kWaves * kRows;   // tokens per item (512)
 constexpr long kSpinLimit = 4000000;   // bounded wait (a few seconds); normal waits are microseconds
 
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
-constexpr int kGather = 8;             // chunk words the leader loads at once
+constexpr int kGather = 4;             // chunk words a gathering thread loads at once
 
 struct Ws {
   int* status;       // [0] time-out flag
@@ -114,6 +118,7 @@ __device__ unsigned short rd_half(double v) {
 
 struct Smem {
   uint32_t red_min[kWaves][16][4], red_max[kWaves][16][4];
+  float part_lo[kWaves * 64 / 128][128], part_hi[kWaves * 64 / 128][128];   // leader's gather
   uint32_t thr[64];                                   // per channel pair: float16 thresholds
 };
 
@@ -181,50 +186,63 @@ __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int 
                             ((uint32_t)__half_as_ushort(__float2half_rn(hi_v)) << 16);
       st_word(w.slot + ((size_t)u * S + s) * 128 + tid, word);
     }
-    if (tid < 128) {
-      uint32_t uw;
-      if (leader) {
-        // gather every chunk's word of channel tid, kGather loads in flight
-        float lo_v = INFINITY, hi_v = -INFINITY;
-        const uint32_t* src = w.slot + (size_t)u * S * 128 + tid;
-        for (int c0 = 0; c0 < S; c0 += kGather) {
-          uint32_t wd[kGather];
-          long spins = 0;
-          for (;;) {
-            bool ready = true;
-#pragma unroll
-            for (int q = 0; q < kGather; ++q) {
-              wd[q] = c0 + q < S ? ld_word(src + (size_t)(c0 + q) * 128) : 0u;
-              ready &= wd[q] != kEmpty;
-            }
-            if (ready) break;
-            __builtin_amdgcn_s_sleep(2);
-            if (++spins > kSpinLimit) {
-              atomicExch(w.status, 1);
-              break;
-            }
-          }
+    uint32_t uw = 0;
+    if (leader) {
+      // every thread gathers: channel tid % 128 over its quarter's chunks,
+      // kGather words per poll, so the whole gather costs one round trip
+      constexpr int Q = kWaves * 64 / 128;
+      const int c = tid & 127, q0 = tid >> 7;
+      float lo_v = INFINITY, hi_v = -INFINITY;
+      const uint32_t* src = w.slot + (size_t)u * S * 128 + c;
+      for (int c0 = q0 * kGather; c0 < S; c0 += Q * kGather) {
+        uint32_t wd[kGather];
+        long spins = 0;
+        for (;;) {
+          bool ready = true;
 #pragma unroll
           for (int q = 0; q < kGather; ++q) {
-            if (c0 + q < S) {
-              lo_v = fminf(lo_v, lo_f(wd[q]));
-              hi_v = fmaxf(hi_v, hi_f(wd[q]));
-            }
+            wd[q] = c0 + q < S ? ld_word(src + (size_t)(c0 + q) * 128) : 0u;
+            ready &= wd[q] != kEmpty;
           }
-        }
-        uw = (uint32_t)__half_as_ushort(__float2half_rn(lo_v)) |
-             ((uint32_t)__half_as_ushort(__float2half_rn(hi_v)) << 16);
-        st_word(w.fin + (size_t)u * 128 + tid, uw);
-      } else {
-        long spins = 0;
-        while ((uw = ld_word(w.fin + (size_t)u * 128 + tid)) == kEmpty) {
+          if (ready) break;
           __builtin_amdgcn_s_sleep(2);
           if (++spins > kSpinLimit) {
             atomicExch(w.status, 1);
             break;
           }
         }
+#pragma unroll
+        for (int q = 0; q < kGather; ++q) {
+          if (c0 + q < S) {
+            lo_v = fminf(lo_v, lo_f(wd[q]));
+            hi_v = fmaxf(hi_v, hi_f(wd[q]));
+          }
+        }
       }
+      sm.part_lo[q0][c] = lo_v;
+      sm.part_hi[q0][c] = hi_v;
+      __syncthreads();
+      if (tid < 128) {
+#pragma unroll
+        for (int q = 1; q < Q; ++q) {
+          lo_v = fminf(lo_v, sm.part_lo[q][tid]);
+          hi_v = fmaxf(hi_v, sm.part_hi[q][tid]);
+        }
+        uw = (uint32_t)__half_as_ushort(__float2half_rn(lo_v)) |
+             ((uint32_t)__half_as_ushort(__float2half_rn(hi_v)) << 16);
+        st_word(w.fin + (size_t)u * 128 + tid, uw);
+      }
+    } else if (tid < 128) {
+      long spins = 0;
+      while ((uw = ld_word(w.fin + (size_t)u * 128 + tid)) == kEmpty) {
+        __builtin_amdgcn_s_sleep(2);
+        if (++spins > kSpinLimit) {
+          atomicExch(w.status, 1);
+          break;
+        }
+      }
+    }
+    if (tid < 128) {
       const float lo_v = lo_f(uw), hi_v = hi_f(uw);
       unsigned short t = rd_half(0.5 * ((double)lo_v + (double)hi_v));
       reinterpret_cast<unsigned short*>(sm.thr)[tid] = t;
@@ -330,7 +348,10 @@ __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int 
                                                   : make_uint4(out[4], out[5], out[6], out[7]);
       }
     }
-    __syncthreads();       // LDS tiles are reused by the next item
+    // No barrier here: the next item writes red_* before, and thr / part_*
+    // only after, a barrier that every thread reaches after its last read of
+    // them in this item, so the LDS reuse is already ordered; the code stores
+    // drain while the next tile loads.
 }
 
 template <int LAYOUT>
@@ -387,7 +408,7 @@ hipError_t quant_fused(const QuantArgs& a) {
   int n = a.n, Sv = S, un = units;
   void* args[] = {(void*)&x, (void*)&n, (void*)&un, (void*)&Sv, (void*)&a.codes, (void*)&a.scale,
                   (void*)&a.minv, (void*)&w};
-  return hipLaunchCooperativeKernel(fn, dim3((unsigned)grid), dim3(kWaves * 64), args, 0, a.stream);
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kWaves * 64), args, 0, a.stream);
 }
 
 }  // namespace cqi

@@ -116,8 +116,10 @@ const char* cq_status_str(cq_status s);
  *             when that is 0).  After the call completes, its first int32 is
  *             a status word: 0, or 1 if a workgroup of the fused path gave up
  *             waiting for the other chunks of its (batch, head) (the outputs
- *             are then invalid; this does not happen when the launch is
- *             co-resident, which the library arranges).
+ *             are then invalid).  The fused path launches no more workgroups
+ *             than the device holds at once; a time-out needs other work to
+ *             keep part of the device busy for seconds.  CQ_PATH_GENERIC has
+ *             no such wait.
  *
  * For each (b, h, channel j) with mn = min_i x, mx = max_i x over the n tokens:
  *   code(i, j) = round-half-to-even((x_ij - mn)*L/(mx - mn)), decided exactly;
