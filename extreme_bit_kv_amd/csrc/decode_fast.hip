@@ -40,6 +40,7 @@ constexpr int kWaves = 16;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 128;
 constexpr int kMaxTail = 256;
+constexpr int kPreTail = 64;          // tail tokens whose loads are issued in the prologue
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -115,15 +116,19 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
   __shared__ uint32_t s_adig[4][3][32];         // K-side A digits: [head][plane][128 channel bytes]
-  __shared__ uint32_t s_pdig[kWaves][4][3][32]; // V-side A digits per wave: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_tmax[4];
+  __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
+  __shared__ float s_tailred[8][4][128];        // tail values per token phase
   // Scores of tiles kRegT..MAXT-1 of each wave, one private 32-byte row per
   // lane (a 16-wave workgroup has 128 registers per lane; the first kRegT
   // tiles stay in registers).  After the value phase the same storage holds
-  // the per-wave value partials.
-  constexpr int kRegT = MAXT == 2 ? 2 : 1;
+  // the per-wave value partials.  With every tile in LDS, a wave stages its
+  // V-side A digits ([head][plane][128 token bytes]) in the score rows of
+  // the tile it has just read; otherwise in s_pdig.
+  constexpr int kRegT = MAXT == 4 ? 0 : MAXT;
+  constexpr bool kPdInSc = kRegT == 0;
+  __shared__ uint32_t s_pdig[kPdInSc ? 1 : kWaves][4][3][32];
   constexpr int kLdsT = MAXT > kRegT ? MAXT - kRegT : 0;
   constexpr int kScBytes = kLdsT * kWaves * 64 * 32;
   constexpr int kRedBytes = kWaves * 4 * 128 * 4;
@@ -195,7 +200,7 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   const int oh = lane >> 4;                     // output lane: head
   const float inv2f = s_inv2f[oh < G ? oh : 0];
   const float c0f = (float)s_c0[oh < G ? oh : 0];
-  float sc[kRegT][8];
+  float sc[kRegT > 0 ? kRegT : 1][8];
   float vmin = INFINITY, vmax = -INFINITY;
   auto load_k = [&](int t, uint4& w0, uint4& w1) {
     const int tile = wave + kWaves * t;
@@ -233,22 +238,83 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       }
     }
     if (t < kRegT) {
+      // pin the finished scores: without this the compiler keeps the four
+      // accumulator registers per token alive instead, and spills
 #pragma unroll
-      for (int m = 0; m < 8; ++m) sc[t < kRegT ? t : 0][m] = st[m];
+      for (int m = 0; m < 8; ++m) {
+        asm volatile("" : "+v"(st[m]));
+        sc[t < kRegT ? t : 0][m] = st[m];
+      }
     } else {
       s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][0] = make_float4(st[0], st[1], st[2], st[3]);
       s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][1] = make_float4(st[4], st[5], st[6], st[7]);
     }
   }
+  // the first value tile is requested before the score statistics settle
+  auto load_v = [&](int t, uint4& w0, uint4& w1) {
+    const int row = (wave + kWaves * t) * 4 + g4;   // V word row of this lane, channels 8*i16 .. +7
+    if (row < R) {
+      const uint4* src = reinterpret_cast<const uint4*>(P.vc + ((size_t)unit * R + row) * 128 + 8 * i16);
+      w0 = src[0];
+      w1 = src[1];
+    } else {
+      w0 = make_uint4(0, 0, 0, 0);
+      w1 = make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 vn0, vn1;
+  load_v(0, vn0, vn1);
+  // ... and so are the first kPreTail tail tokens: keys as (token
+  // 4 wave + lane/16, channels 8 (lane%16) ..+7), values as (channel
+  // tid%128, tokens tid/128 + 8i).
+  const int tsub = lane >> 4, tcl = lane & 15;
+  uint4 ktp0 = make_uint4(0, 0, 0, 0), ktp1 = make_uint4(0, 0, 0, 0);
+  {
+    const int j = 4 * wave + tsub;
+    if (j < T) {
+      if (P.tail_f32) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(P.kt) +
+                                                          ((size_t)unit * T + j) * 128 + 8 * tcl);
+        ktp0 = src[0];
+        ktp1 = src[1];
+      } else {
+        ktp0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
+                                               ((size_t)unit * T + j) * 128 + 8 * tcl);
+      }
+    }
+  }
+  const int vtj = tid & 127, vtq = tid >> 7;
+  float vtp[kPreTail / 8];
+#pragma unroll
+  for (int i = 0; i < kPreTail / 8; ++i) {
+    const int t = vtq + 8 * i;
+    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, P.tail_f32) : 0.f;
+  }
   // ---- text tail scores ---------------------------------------------------
   {
-    const int sub = lane >> 4, cl = lane & 15;
+    const int sub = tsub, cl = tcl;
     for (int j0 = 4 * wave; j0 < T; j0 += 4 * kWaves) {
       const int j = j0 + sub;
       float kf[8];
+      if (j0 == 4 * wave) {                     // prefetched in the prologue
+        if (P.tail_f32) {
+          kf[0] = __uint_as_float(ktp0.x); kf[1] = __uint_as_float(ktp0.y);
+          kf[2] = __uint_as_float(ktp0.z); kf[3] = __uint_as_float(ktp0.w);
+          kf[4] = __uint_as_float(ktp1.x); kf[5] = __uint_as_float(ktp1.y);
+          kf[6] = __uint_as_float(ktp1.z); kf[7] = __uint_as_float(ktp1.w);
+        } else {
+          const uint32_t hw[4] = {ktp0.x, ktp0.y, ktp0.z, ktp0.w};
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, P.tail_f32) : 0.f;
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, P.tail_f32) : 0.f;
+      }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float s = 0.f;
@@ -300,10 +366,40 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
     }
   }
   __syncthreads();
-  // tail probabilities (in place)
-  for (int i = tid; i < G * T; i += kThreads) {
-    const int hh = i / T, j = i % T;
-    s_ts[hh][j] = exp2f((s_ts[hh][j] - s_tmax[hh]) * kLog2e);
+  // tail probabilities (in place) and their sum, wave hh for head hh
+  if (wave < G) {
+    const int hh = wave;
+    const float top = s_tmax[hh];
+    float pt = 0.f;
+    for (int j = lane; j < T; j += 64) {
+      const float pj = exp2f((s_ts[hh][j] - top) * kLog2e);
+      s_ts[hh][j] = pj;
+      pt += pj;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
+    if (lane == 0) s_ptail[hh] = pt;
+  }
+  __syncthreads();
+  // text-tail values: thread (channel vtj, phase vtq) sums the tail tokens
+  // vtq + 8i for every head, the first kPreTail from the prologue's loads
+  {
+    float ta[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kPreTail / 8; ++i) {
+      const int t = vtq + 8 * i;
+      if (t < T) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], vtp[i], ta[hh]);
+      }
+    }
+    for (int t = kPreTail + vtq; t < T; t += 8) {
+      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, P.tail_f32);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], v, ta[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) s_tailred[vtq][hh][vtj] = ta[hh];
   }
 
   // ---- phase 2: values ------------------------------------------------------
@@ -312,20 +408,6 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
   float psum = 0.f;
-  unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
-  auto load_v = [&](int t, uint4& w0, uint4& w1) {
-    const int row = (wave + kWaves * t) * 4 + g4;   // V word row of this lane, channels 8*i16 .. +7
-    if (row < R) {
-      const uint4* src = reinterpret_cast<const uint4*>(P.vc + ((size_t)unit * R + row) * 128 + 8 * i16);
-      w0 = src[0];
-      w1 = src[1];
-    } else {
-      w0 = make_uint4(0, 0, 0, 0);
-      w1 = make_uint4(0, 0, 0, 0);
-    }
-  };
-  uint4 vn0, vn1;
-  load_v(0, vn0, vn1);
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     const int tile = wave + kWaves * t;
@@ -343,6 +425,10 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       st[0] = a0.x; st[1] = a0.y; st[2] = a0.z; st[3] = a0.w;
       st[4] = a1.x; st[5] = a1.y; st[6] = a1.z; st[7] = a1.w;
     }
+    // the wave's lanes have read their rows above; LDS keeps a wave's
+    // accesses in order, so the digits may now overwrite them
+    unsigned char* pd = kPdInSc ? reinterpret_cast<unsigned char*>(&s_sc[t >= kRegT ? t - kRegT : 0][wave][0][0])
+                                : reinterpret_cast<unsigned char*>(&s_pdig[kPdInSc ? 0 : wave][0][0][0]);
     uint32_t fb[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -398,33 +484,6 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
   __syncthreads();
-  // text-tail values: thread (half, head, channel) sums every other tail
-  // token, 16 independent loads in flight
-  __shared__ float s_tail[2][4][128];
-  __shared__ float s_ptail[2][4];
-  {
-    const int half = tid >> 9, hh = (tid >> 7) & 3, j = tid & 127;
-    float tail = 0.f, pt = 0.f;
-    if (hh < G) {
-      for (int t0 = half; t0 < T; t0 += 32) {
-        float vv[16], pp[16];
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          const int t = t0 + 2 * q;
-          vv[q] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + j, P.tail_f32) : 0.f;
-          pp[q] = t < T ? s_ts[hh][t] : 0.f;
-        }
-#pragma unroll
-        for (int q = 0; q < 16; ++q) {
-          pt += pp[q];
-          tail = fmaf(pp[q], vv[q], tail);
-        }
-      }
-    }
-    s_tail[half][hh][j] = tail;
-    if (j == 0) s_ptail[half][hh] = pt;
-  }
-  __syncthreads();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     float sv = 0.f, pv = 0.f;
@@ -433,8 +492,10 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       sv += s_vred[w][hh][j];
       pv += s_psum[w][hh];
     }
-    const float tail = s_tail[0][hh][j] + s_tail[1][hh][j];
-    const float pt = s_ptail[0][hh] + s_ptail[1][hh];
+    float tail = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) tail += s_tailred[q][hh][j];
+    const float pt = T > 0 ? s_ptail[hh] : 0.f;
     float o = tail;
     if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
     o /= (pv + pt);
