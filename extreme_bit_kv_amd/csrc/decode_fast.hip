@@ -6,8 +6,10 @@
 // integer codes enter the products; part 3: the visual scores of each query
 // head are mapped by the affine g fixed by their min and max before softmax.
 //
-// One workgroup (16 waves) per (batch, kv head); its query heads (G <= 4)
-// share every code it reads.  A wave owns 128-token tiles.
+// One workgroup (8 waves) per (batch, kv head); its query heads (G <= 4)
+// share every code it reads.  A wave owns 128-token tiles.  Two workgroups
+// fit on a CU, so a whole decode step (every unit of the batch) is resident
+// at once and one unit's reductions overlap another's loads.
 //
 // K side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16] with
 // v_mfma_i32_16x16x64_i8, twice (128 channels).  Rows of A are
@@ -18,8 +20,10 @@
 // (w >> s) & 0x01010101, which yields channels 4s..4s+3 of the word's group
 // thanks to the interleaved packed layout.  Each lane ends up holding all
 // planes of one (head, token) score: s = (a0 + 256 a1 + 65536 a2) 2^-F + c0.
-// The scores stay in registers until the workgroup knows every head's min and
-// max, which fix g.
+// The first pass over the keys only gathers every head's min and max, which
+// fix g; the value pass reads the key tiles again (they are still in the
+// Infinity Cache) and recomputes the same scores, exactly, instead of keeping
+// 4 B per head and token on chip.
 //
 // V side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16], rows again
 // (head, plane), columns channels, contraction over tokens.  p = exp(g(s) -
@@ -36,11 +40,11 @@
 
 namespace {
 
-constexpr int kWaves = 16;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 128;
 constexpr int kMaxTail = 256;
-constexpr int kPreTail = 64;          // tail tokens whose loads are issued in the prologue
+constexpr int kPreTail = 64;          // tail tokens whose loads are issued early
 constexpr float kLog2e = 1.4426950408889634f;
 
 typedef int v4i __attribute__((ext_vector_type(4)));
@@ -101,8 +105,10 @@ __device__ __forceinline__ void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-template <int G, int MAXT>
-__global__ void __launch_bounds__(kThreads) df_b1(Params P) {
+// F32: query and text tail are float32 (else float16); the fast path takes
+// them in one dtype.
+template <int G, int MAXT, bool F32>
+__global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int unit = blockIdx.x;
   const int b = unit / P.Hkv, h = unit % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -116,36 +122,43 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
   __shared__ uint32_t s_adig[4][3][32];         // K-side A digits: [head][plane][128 channel bytes]
+  __shared__ uint32_t s_pdig[kWaves][4][3][32]; // V-side A digits per wave: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
-  __shared__ float s_tailred[8][4][128];        // tail values per token phase
-  // Scores of tiles kRegT..MAXT-1 of each wave, one private 32-byte row per
-  // lane (a 16-wave workgroup has 128 registers per lane; the first kRegT
-  // tiles stay in registers).  After the value phase the same storage holds
-  // the per-wave value partials.  With every tile in LDS, a wave stages its
-  // V-side A digits ([head][plane][128 token bytes]) in the score rows of
-  // the tile it has just read; otherwise in s_pdig.
-  constexpr int kRegT = MAXT == 4 ? 0 : MAXT;
-  constexpr bool kPdInSc = kRegT == 0;
-  __shared__ uint32_t s_pdig[kPdInSc ? 1 : kWaves][4][3][32];
-  constexpr int kLdsT = MAXT > kRegT ? MAXT - kRegT : 0;
-  constexpr int kScBytes = kLdsT * kWaves * 64 * 32;
-  constexpr int kRedBytes = kWaves * 4 * 128 * 4;
-  __shared__ float4 s_big[(kScBytes > kRedBytes ? kScBytes : kRedBytes) / 16];
-  float4 (*s_sc)[kWaves][64][2] = reinterpret_cast<float4 (*)[kWaves][64][2]>(s_big);
-  float (*s_vred)[4][128] = reinterpret_cast<float (*)[4][128]>(s_big);
+  __shared__ float s_tailred[kThreads / 128][4][128];   // tail values per token phase
+  __shared__ float s_vred[kWaves][4][128];      // per-wave value partials
   __shared__ float s_psum[kWaves][4];
+
+  // operand coordinates of the 16 x 16 x 64 products
+  const int i16 = lane & 15, g4 = lane >> 4;    // A/B operand lane coordinates
+  const int rh = i16 >> 2, rp = i16 & 3;        // A row = (head rh, plane rp)
+  const int oh = lane >> 4;                     // output lane: head
+  const uint32_t* kc = P.kc;
+  auto load_k = [&](int t, uint4& w0, uint4& w1) {
+    const int tile = wave + kWaves * t;
+    const int tok = tile * kTile + 8 * i16;
+    if (tile < ntiles && tok < n) {
+      const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
+      w0 = src[0];
+      w1 = src[1];
+    } else {
+      w0 = make_uint4(0, 0, 0, 0);
+      w1 = make_uint4(0, 0, 0, 0);
+    }
+  };
+  uint4 kn0, kn1;                               // one key tile of look-ahead,
+  load_k(0, kn0, kn1);                          // the first one under the prologue
 
   // ---- prologue: post-scaled query, fixed-point digits -------------------
   __shared__ double s_c0p[8];
   __shared__ float s_mqp[8];
-  if (tid < 4 * 128) {                          // waves 0..7: head = wave / 2
+  {                                             // thread: head tid / 128, channel tid % 128
     const int hh = tid >> 7, j = tid & 127;
     float qv = 0.f, qp = 0.f;
     double pr = 0.0;
     if (hh < G) {
-      qv = P.sm * ld_any(P.q, ((size_t)b * P.Hq + h * G + hh) * 128 + j, P.q_f32);
+      qv = P.sm * ld_any(P.q, ((size_t)b * P.Hq + h * G + hh) * 128 + j, F32);
       qp = qv * P.ks[(size_t)unit * 128 + j];
       pr = (double)qv * (double)P.km[(size_t)unit * 128 + j];
     }
@@ -173,7 +186,7 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
     s_c0[tid] = c0;
   }
   __syncthreads();
-  if (tid < 4 * 128) {
+  {
     const int hh = tid >> 7, j = tid & 127;
     const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
     const int d0 = ((Q + 128) & 255) - 128;
@@ -187,9 +200,7 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   }
   __syncthreads();
 
-  // ---- phase 1: visual scores ------------------------------------------
-  const int i16 = lane & 15, g4 = lane >> 4;     // A/B operand lane coordinates
-  const int rh = i16 >> 2, rp = i16 & 3;        // A row = (head rh, plane rp)
+  // ---- phase 1: visual scores, their min and max -------------------------
   v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
   if (rp < 3 && rh < G) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
@@ -197,60 +208,54 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
     ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
     ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
   }
-  const int oh = lane >> 4;                     // output lane: head
   const float inv2f = s_inv2f[oh < G ? oh : 0];
   const float c0f = (float)s_c0[oh < G ? oh : 0];
-  float sc[kRegT > 0 ? kRegT : 1][8];
-  float vmin = INFINITY, vmax = -INFINITY;
-  auto load_k = [&](int t, uint4& w0, uint4& w1) {
-    const int tile = wave + kWaves * t;
-    const int tok = tile * kTile + 8 * i16;
-    if (tile < ntiles && tok < n) {
-      const uint4* src = reinterpret_cast<const uint4*>(P.kc + ((size_t)unit * 4 + g4) * n + tok);
-      w0 = src[0];
-      w1 = src[1];
-    } else {
-      w0 = make_uint4(0, 0, 0, 0);
-      w1 = make_uint4(0, 0, 0, 0);
-    }
-  };
-  uint4 kn0, kn1;                               // one tile of look-ahead
-  load_k(0, kn0, kn1);
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    const int tile = wave + kWaves * t;
-    const uint32_t wd[8] = {kn0.x, kn0.y, kn0.z, kn0.w, kn1.x, kn1.y, kn1.z, kn1.w};
-    if (t + 1 < MAXT) load_k(t + 1, kn0, kn1);
-    const int tokb = tile * kTile + 8 * (lane & 15);   // this lane's output tokens tokb + m
-    float st[8];
+  // scores of this lane's 8 tokens (head oh) from one key tile; the same
+  // integer products and the same rounding in both passes
+  auto scores = [&](const uint4& w0, const uint4& w1, float (&st)[8]) {
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       v4i acc = {0, 0, 0, 0};
       acc = mfma(ak0, spread_lo(wd[m]), acc);
       acc = mfma(ak1, spread_hi(wd[m]), acc);
       const int dot = acc[0] + (acc[1] << 8) + (acc[2] << 16);
-      const float s = fmaf((float)dot, inv2f, c0f);
-      const bool valid = tile < ntiles && tokb + m < n;
-      st[m] = s;
-      if (valid) {
-        vmin = fminf(vmin, s);
-        vmax = fmaxf(vmax, s);
-      }
+      st[m] = fmaf((float)dot, inv2f, c0f);
+      // pin the finished score: otherwise the compiler may keep the four
+      // accumulator registers alive in its place
+      asm volatile("" : "+v"(st[m]));
     }
-    if (t < kRegT) {
-      // pin the finished scores: without this the compiler keeps the four
-      // accumulator registers per token alive instead, and spills
+  };
+  float vmin = INFINITY, vmax = -INFINITY;
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        asm volatile("" : "+v"(st[m]));
-        sc[t < kRegT ? t : 0][m] = st[m];
-      }
-    } else {
-      s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][0] = make_float4(st[0], st[1], st[2], st[3]);
-      s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][1] = make_float4(st[4], st[5], st[6], st[7]);
+  for (int t = 0; t < MAXT; ++t) {
+    const int tile = wave + kWaves * t;
+    const uint4 kw0 = kn0, kw1 = kn1;
+    if (t + 1 < MAXT) load_k(t + 1, kn0, kn1);
+    // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
+    const bool ok = tile < ntiles && tile * kTile + 8 * i16 < n;
+    float st[8];
+    scores(kw0, kw1, st);
+    float tmin = st[0], tmax = st[0];
+#pragma unroll
+    for (int m = 1; m < 8; ++m) {
+      tmin = fminf(tmin, st[m]);
+      tmax = fmaxf(tmax, st[m]);
     }
+    if (ok) {
+      vmin = fminf(vmin, tmin);
+      vmax = fmaxf(vmax, tmax);
+    }
+    // fold tile by tile: left free, the compiler sinks these updates past the
+    // loop and keeps every tile's scores alive
+    asm volatile("" : "+v"(vmin), "+v"(vmax));
   }
-  // the first value tile is requested before the score statistics settle
+  // the first key and value tiles of the second pass are requested before the
+  // score statistics settle ...  (The key base goes through an opaque copy:
+  // otherwise the compiler proves the second pass's loads equal the first's and
+  // keeps every first-pass score alive instead of recomputing it.)
+  asm("" : "+s"(kc));
+  load_k(0, kn0, kn1);
   auto load_v = [&](int t, uint4& w0, uint4& w1) {
     const int row = (wave + kWaves * t) * 4 + g4;   // V word row of this lane, channels 8*i16 .. +7
     if (row < R) {
@@ -265,39 +270,48 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   uint4 vn0, vn1;
   load_v(0, vn0, vn1);
   // ... and so are the first kPreTail tail tokens: keys as (token
-  // 4 wave + lane/16, channels 8 (lane%16) ..+7), values as (channel
-  // tid%128, tokens tid/128 + 8i).
+  // 4 wave + lane/16 + 32 r, channels 8 (lane%16) ..+7), values as (channel
+  // tid%128, tokens tid/128 + 4i).
   const int tsub = lane >> 4, tcl = lane & 15;
-  uint4 ktp0 = make_uint4(0, 0, 0, 0), ktp1 = make_uint4(0, 0, 0, 0);
-  {
-    const int j = 4 * wave + tsub;
+  constexpr int kKtRounds = kPreTail / (4 * kWaves);
+  uint4 ktp[kKtRounds][2];
+#pragma unroll
+  for (int r = 0; r < kKtRounds; ++r) {
+    const int j = 4 * wave + tsub + 4 * kWaves * r;
+    ktp[r][0] = make_uint4(0, 0, 0, 0);
+    ktp[r][1] = make_uint4(0, 0, 0, 0);
     if (j < T) {
-      if (P.tail_f32) {
+      if constexpr (F32) {
         const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(P.kt) +
                                                           ((size_t)unit * T + j) * 128 + 8 * tcl);
-        ktp0 = src[0];
-        ktp1 = src[1];
+        ktp[r][0] = src[0];
+        ktp[r][1] = src[1];
       } else {
-        ktp0 = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
-                                               ((size_t)unit * T + j) * 128 + 8 * tcl);
+        ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
+                                                    ((size_t)unit * T + j) * 128 + 8 * tcl);
       }
     }
   }
+  constexpr int kPhases = kThreads / 128;
   const int vtj = tid & 127, vtq = tid >> 7;
-  float vtp[kPreTail / 8];
+  float vtp[kPreTail / kPhases];
 #pragma unroll
-  for (int i = 0; i < kPreTail / 8; ++i) {
-    const int t = vtq + 8 * i;
-    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, P.tail_f32) : 0.f;
+  for (int i = 0; i < kPreTail / kPhases; ++i) {
+    const int t = vtq + kPhases * i;
+    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32) : 0.f;
   }
   // ---- text tail scores ---------------------------------------------------
   {
     const int sub = tsub, cl = tcl;
-    for (int j0 = 4 * wave; j0 < T; j0 += 4 * kWaves) {
+#pragma unroll
+    for (int r = 0; r < kMaxTail / (4 * kWaves); ++r) {
+      const int j0 = 4 * wave + 4 * kWaves * r;
+      if (j0 >= T) break;
       const int j = j0 + sub;
       float kf[8];
-      if (j0 == 4 * wave) {                     // prefetched in the prologue
-        if (P.tail_f32) {
+      if (r < kKtRounds) {                      // requested above
+        const uint4 ktp0 = ktp[r < kKtRounds ? r : 0][0], ktp1 = ktp[r < kKtRounds ? r : 0][1];
+        if constexpr (F32) {
           kf[0] = __uint_as_float(ktp0.x); kf[1] = __uint_as_float(ktp0.y);
           kf[2] = __uint_as_float(ktp0.z); kf[3] = __uint_as_float(ktp0.w);
           kf[4] = __uint_as_float(ktp1.x); kf[5] = __uint_as_float(ktp1.y);
@@ -313,7 +327,7 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       } else {
 #pragma unroll
         for (int c = 0; c < 8; ++c)
-          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, P.tail_f32) : 0.f;
+          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
       }
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
@@ -351,25 +365,19 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       M = fmaxf(M, __shfl_xor(M, off));
       tmax = fmaxf(tmax, __shfl_xor(tmax, off));
     }
+    float lam = 1.f, mu = 0.f, vis_max = M;
+    if (P.calib_on && n > 0) {
+      const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
+      lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
+      mu = t_lo - lam * m;
+      vis_max = fmaxf(t_lo, t_hi);
+    }
+    const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
     if (lane == 0) {
-      float lam = 1.f, mu = 0.f, vis_max = M;
-      if (P.calib_on && n > 0) {
-        const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
-        lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
-        mu = t_lo - lam * m;
-        vis_max = fmaxf(t_lo, t_hi);
-      }
-      const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
       s_lam[hh] = lam * kLog2e;                 // p = 2^(s * lam' + mu')
       s_mu[hh] = (mu - top) * kLog2e;
-      s_tmax[hh] = top;
     }
-  }
-  __syncthreads();
-  // tail probabilities (in place) and their sum, wave hh for head hh
-  if (wave < G) {
-    const int hh = wave;
-    const float top = s_tmax[hh];
+    // tail probabilities (in place) and their sum
     float pt = 0.f;
     for (int j = lane; j < T; j += 64) {
       const float pj = exp2f((s_ts[hh][j] - top) * kLog2e);
@@ -382,19 +390,19 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   }
   __syncthreads();
   // text-tail values: thread (channel vtj, phase vtq) sums the tail tokens
-  // vtq + 8i for every head, the first kPreTail from the prologue's loads
+  // vtq + kPhases i for every head, the first kPreTail from the loads above
   {
     float ta[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < kPreTail / 8; ++i) {
-      const int t = vtq + 8 * i;
+    for (int i = 0; i < kPreTail / kPhases; ++i) {
+      const int t = vtq + kPhases * i;
       if (t < T) {
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], vtp[i], ta[hh]);
       }
     }
-    for (int t = kPreTail + vtq; t < T; t += 8) {
-      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, P.tail_f32);
+    for (int t = kPreTail + vtq; t < T; t += kPhases) {
+      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32);
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], v, ta[hh]);
     }
@@ -408,32 +416,25 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
   float psum = 0.f;
+  unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
 #pragma unroll
   for (int t = 0; t < MAXT; ++t) {
     const int tile = wave + kWaves * t;
     if (tile >= ntiles) break;
-    const uint4 vw0 = vn0, vw1 = vn1;
-    if (t + 1 < MAXT) load_v(t + 1, vn0, vn1);
-    // probabilities of this lane's 8 tokens (head oh), as 22-bit fixed point
-    const int tokb = tile * kTile + 8 * (lane & 15);
-    float st[8];
-    if (t < kRegT) {
-#pragma unroll
-      for (int m = 0; m < 8; ++m) st[m] = sc[t < kRegT ? t : 0][m];
-    } else {
-      const float4 a0 = s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][0], a1 = s_sc[t >= kRegT ? t - kRegT : 0][wave][lane][1];
-      st[0] = a0.x; st[1] = a0.y; st[2] = a0.z; st[3] = a0.w;
-      st[4] = a1.x; st[5] = a1.y; st[6] = a1.z; st[7] = a1.w;
+    const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
+    if (t + 1 < MAXT) {
+      load_k(t + 1, kn0, kn1);
+      load_v(t + 1, vn0, vn1);
     }
-    // the wave's lanes have read their rows above; LDS keeps a wave's
-    // accesses in order, so the digits may now overwrite them
-    unsigned char* pd = kPdInSc ? reinterpret_cast<unsigned char*>(&s_sc[t >= kRegT ? t - kRegT : 0][wave][0][0])
-                                : reinterpret_cast<unsigned char*>(&s_pdig[kPdInSc ? 0 : wave][0][0][0]);
+    // probabilities of this lane's 8 tokens (head oh), as 22-bit fixed point
+    const bool ok = oh < G && tile * kTile + 8 * i16 < n;
+    float st[8];
+    scores(kw0, kw1, st);
     uint32_t fb[8];
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       float p = 0.f;
-      if (oh < G && tokb + m < n) p = exp2f(fmaf(st[m], lam2, mu2));
+      if (ok) p = exp2f(fmaf(st[m], lam2, mu2));
       psum += p;
       fb[m] = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) ^ 0x00008080u;   // bytes: P^0x80, (P>>8)^0x80, P>>16
     }
@@ -442,7 +443,7 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
       for (int pl = 0; pl < 3; ++pl) {
         const uint32_t d0 = gather_byte(fb[0], fb[1], fb[2], fb[3], pl);
         const uint32_t d1 = gather_byte(fb[4], fb[5], fb[6], fb[7], pl);
-        *reinterpret_cast<uint2*>(pd + (oh * 3 + pl) * 128 + 8 * (lane & 15)) = make_uint2(d0, d1);
+        *reinterpret_cast<uint2*>(pd + (oh * 3 + pl) * 128 + 8 * i16) = make_uint2(d0, d1);
       }
     }
     wave_sync_lds();
@@ -471,7 +472,6 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   }
 
   // ---- combine planes, reduce over waves --------------------------------
-  __syncthreads();                          // every wave is done with the score rows
   // lane (head oh, column i16): channels 8*i16 + ct
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
@@ -494,8 +494,8 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
     }
     float tail = 0.f;
 #pragma unroll
-    for (int q = 0; q < 8; ++q) tail += s_tailred[q][hh][j];
-    const float pt = T > 0 ? s_ptail[hh] : 0.f;
+    for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
+    const float pt = s_ptail[hh];
     float o = tail;
     if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
     o /= (pv + pt);
@@ -505,13 +505,21 @@ __global__ void __launch_bounds__(kThreads) df_b1(Params P) {
   }
 }
 
-template <int G>
+template <int G, bool F32>
 hipError_t launch_g(const Params& p, int maxt, int units, hipStream_t st) {
   switch (maxt) {
-    case 1: CQ_LAUNCH((df_b1<G, 1>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-    case 2: CQ_LAUNCH((df_b1<G, 2>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-    default: CQ_LAUNCH((df_b1<G, 4>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
+    case 1: CQ_LAUNCH((df_b1<G, 1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
+    case 2: CQ_LAUNCH((df_b1<G, 2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
+    case 4: CQ_LAUNCH((df_b1<G, 4, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
+    default: CQ_LAUNCH((df_b1<G, 8, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
   }
+}
+
+template <bool F32>
+hipError_t launch_f(const Params& p, int G, int maxt, int units, hipStream_t st) {
+  if (G == 1) return launch_g<1, F32>(p, maxt, units, st);
+  if (G == 2) return launch_g<2, F32>(p, maxt, units, st);
+  return launch_g<4, F32>(p, maxt, units, st);
 }
 
 }  // namespace
@@ -524,7 +532,7 @@ bool decode_fast_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
   const int tiles = (a.n + kTile - 1) / kTile;
   return a.bits == 1 && a.d == 128 && (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 &&
-         tiles <= 4 * kWaves && a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
+         tiles <= 8 * kWaves && a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
 }
 
 hipError_t decode_fast(const DecodeArgs& a) {
@@ -534,11 +542,10 @@ hipError_t decode_fast(const DecodeArgs& a) {
            a.Hq, a.Hkv, a.n, a.T, a.q_dtype == CQ_F32, a.tail_dtype == CQ_F32, a.out_dtype == CQ_F32,
            a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi};
   const int tiles = (a.n + kTile - 1) / kTile;
-  const int maxt = tiles <= kWaves ? 1 : (tiles <= 2 * kWaves ? 2 : 4);
+  const int maxt = tiles <= kWaves ? 1 : (tiles <= 2 * kWaves ? 2 : (tiles <= 4 * kWaves ? 4 : 8));
   const int G = a.Hq / a.Hkv;
-  if (G == 1) return launch_g<1>(p, maxt, units, a.stream);
-  if (G == 2) return launch_g<2>(p, maxt, units, a.stream);
-  return launch_g<4>(p, maxt, units, a.stream);
+  return a.q_dtype == CQ_F32 ? launch_f<true>(p, G, maxt, units, a.stream)
+                             : launch_f<false>(p, G, maxt, units, a.stream);
 }
 
 }  // namespace cqi

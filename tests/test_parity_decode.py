@@ -184,10 +184,11 @@ def test_bit_width_sweep_sampled(bits):
     _compare(got, _oracle(K, V, q, kt, vt, bits, None, [(0, 1), (31, 6)]), 4)
 
 
-@pytest.mark.parametrize("n", [32, 96, 128, 2048, 2080, 4096, 4224, 8192])
+@pytest.mark.parametrize("n", [32, 96, 128, 1024, 1152, 2048, 2080, 4096, 4224, 8192])
 @pytest.mark.parametrize("G", [1, 2, 4])
 def test_fast_kernel_tile_counts(n, G):
-    """Every register/LDS split of the matrix-core kernel (1, 2 and 4 tiles per wave), ragged tiles."""
+    """Every instantiation of the matrix-core kernel (1, 2, 4 and 8 tiles per wave) on both sides of
+    each boundary, ragged tiles included."""
     K, V, q, kt, vt = draw_inputs(1, 2 * G, 2, n, 64, seed=n + G)
     note(f"decode fast n={n} G={G}")
     got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST)
