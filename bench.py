@@ -16,6 +16,14 @@ tokens, the roofline of each kernel, and the CPU oracle timed on a bounded
 sample of the same workload (the ``cpu_baseline`` leg; the only place this
 file touches the oracle).
 
+Sweeps (not the headline line; one JSON line per point, then a table):
+    --sweeps               bit-width sweep (b = 1, 2, 4, 8 and the fp16
+                           baseline at B=32, n=3328, one layer) and the
+                           memory-budget sweep (32-layer stacks at the
+                           largest batch that fits 5/10/20/30 GiB of KV cache
+                           at 1 bit and at fp16, n = 3328 and 8192, one full
+                           decode step over all layers)
+
 Profiling helpers (used to produce profiles/):
     --only {step,copy}     run only the timed steps, or only a 1 GiB copy
                            kernel (the HBM-counter calibration reference)
@@ -57,6 +65,14 @@ def decode_bytes(cfg):
     G = cfg.Hq // cfg.Hkv
     per = 2 * cfg.n * cfg.d * cfg.bits // 8 + 2 * cfg.T * cfg.d * 2 + 4 * cfg.d * 4 + 2 * G * cfg.d * 2
     return units * per
+
+
+def cache_bytes_per_seq(n, T, Hkv, d, bits, layers):
+    """KV cache bytes one sequence holds over `layers` layers: 1-bit codes plus fp32
+    scale/min plus the fp16 tail (bits > 0), or the plain fp16 cache (bits == 0)."""
+    if bits == 0:
+        return layers * Hkv * 2 * (n + T) * d * 2
+    return layers * Hkv * (2 * n * d * bits // 8 + 2 * T * d * 2 + 4 * d * 4)
 
 
 def fp16_bytes(cfg):
@@ -293,6 +309,142 @@ def run(args):
 
 
 # ---------------------------------------------------------------------------
+# sweeps: bit widths (one layer) and KV-memory budgets (32-layer stacks)
+# ---------------------------------------------------------------------------
+
+def sweeps(args):
+    import numpy as np
+    import torch
+
+    import extreme_bit_kv_amd as cqb
+    from workloads import CONFIGS, ROLE_K, ROLE_KTAIL, ROLE_V, ROLE_VTAIL, Config, kv_torch, q_torch
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    sm = 1.0 / float(np.sqrt(128.0))
+    rows = []
+
+    def note(msg):
+        print(f"[sweeps] {msg}", file=sys.stderr, flush=True)
+
+    def timed(fn, reps, flush=None):
+        ts = []
+        for _ in range(3):
+            fn()
+        for _ in range(reps):
+            if flush is not None:
+                flush.zero_()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            ts.append((a, b))
+        torch.cuda.synchronize()
+        return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
+
+    def emit(row):
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+
+    # -- bit-width sweep: one layer, B=32, n=3328, decode with the Infinity Cache flushed
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    base = CONFIGS["bits_sweep_b1"]
+    K = kv_torch(base.seed, 0, ROLE_K, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+    V = kv_torch(base.seed, 0, ROLE_V, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+    kt = kv_torch(base.seed, 0, ROLE_KTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
+    vt = kv_torch(base.seed, 0, ROLE_VTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
+    q = q_torch(base.seed, 0, base.B, base.Hq, base.d, base.dtype, dev)
+    out = torch.empty((base.B, base.Hq, base.d), dtype=torch.float16, device=dev)
+    for bits in (1, 2, 4, 8):
+        cfg = CONFIGS[f"bits_sweep_b{bits}"]
+        note(f"bit sweep b={bits}")
+        kc, ks, km = cqb.cq_quantize_kv(K, bits, cqb.CQ_LAYOUT_K)
+        vc, vs, vm = cqb.cq_quantize_kv(V, bits, cqb.CQ_LAYOUT_V)
+        ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d, bits)),
+                         dtype=torch.uint8, device=dev)
+        t = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=bits, sm_scale=sm,
+                                             calib=cfg.calib, out=out, workspace=ws), args.steps, scratch)
+        nb = decode_bytes(cfg)
+        emit({"sweep": "bits", "bits": bits, "B": cfg.B, "n": cfg.n, "T": cfg.T, "calib": cfg.calib is not None,
+              "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(cfg.B / t, 1),
+              "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del kc, ks, km, vc, vs, vm, ws
+    Kf, Vf = torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)
+    fws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(base.B, base.Hq, base.Hkv, base.n + base.T,
+                                                                   base.d)), dtype=torch.uint8, device=dev)
+    note("bit sweep fp16 baseline")
+    t = timed(lambda: cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=fws), args.steps, scratch)
+    nb = fp16_bytes(base)
+    emit({"sweep": "bits", "bits": 16, "B": base.B, "n": base.n, "T": base.T, "calib": False,
+          "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(base.B / t, 1),
+          "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+    del K, V, kt, vt, q, out, Kf, Vf, fws, scratch
+    torch.cuda.empty_cache()
+
+    # -- memory-budget sweep: 32 layers, the largest batch whose cache fits the budget
+    layers, Hq, Hkv, d, T = 32, 32, 8, 128, 64
+    calib = (0.9, 0.0, 0.8, 0.0)
+    for n in (3328, 8192):
+        for gib in (5, 10, 20, 30):
+            budget = gib << 30
+            for bits in (1, 0):
+                per_seq = cache_bytes_per_seq(n, T, Hkv, d, bits, layers)
+                B = budget // per_seq
+                note(f"budget {gib} GiB n={n} {'1-bit' if bits else 'fp16'}: batch {B}, building {layers} layers")
+                cache = []
+                for layer in range(layers):
+                    seed = 5
+                    K = kv_torch(seed, layer, ROLE_K, B, Hkv, n, d, "float16", dev)
+                    V = kv_torch(seed, layer, ROLE_V, B, Hkv, n, d, "float16", dev)
+                    kt = kv_torch(seed, layer, ROLE_KTAIL, B, Hkv, T, d, "float16", dev)
+                    vt = kv_torch(seed, layer, ROLE_VTAIL, B, Hkv, T, d, "float16", dev)
+                    q = q_torch(seed, layer, B, Hq, d, "float16", dev)
+                    if bits:
+                        kc = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
+                        vc = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
+                        cache.append((q, kc, vc, kt, vt))
+                    else:
+                        cache.append((q, torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)))
+                    del K, V
+                out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+                if bits:
+                    ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, 1)),
+                                     dtype=torch.uint8, device=dev)
+
+                    def step():
+                        for (q, (kc, ks, km), (vc, vs, vm), kt, vt) in cache:
+                            cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=1, sm_scale=sm,
+                                               calib=calib, out=out, workspace=ws)
+                    nb = layers * B * Hkv * (2 * n * d // 8 + 2 * T * d * 2 + 4 * d * 4 + 2 * (Hq // Hkv) * d * 2)
+                else:
+                    ws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(B, Hq, Hkv, n + T, d)),
+                                     dtype=torch.uint8, device=dev)
+
+                    def step():
+                        for (q, Kf, Vf) in cache:
+                            cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=ws)
+                    nb = layers * B * Hkv * (2 * (n + T) * d * 2 + 2 * (Hq // Hkv) * d * 2)
+                t = timed(step, max(3, args.steps // 4))
+                emit({"sweep": "budget", "budget_GiB": gib, "n": n, "T": T, "layers": layers,
+                      "cache": "1-bit" if bits else "fp16", "B": int(B), "step_ms": round(t * 1e3, 4),
+                      "seq_steps_per_s": round(B / t, 1), "GBs": round(nb / t / 1e9, 1),
+                      "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+                del cache, out, ws
+                torch.cuda.empty_cache()
+
+    # table
+    print("\n| sweep | point | B | ms | seq-steps/s | GB/s | of 8 TB/s |", file=sys.stderr)
+    print("|---|---|---|---|---|---|---|", file=sys.stderr)
+    for r in rows:
+        if r["sweep"] == "bits":
+            pt, ms = (f"b={r['bits']}" if r["bits"] < 16 else "fp16") + f", n={r['n']}", r["decode_ms"]
+        else:
+            pt, ms = f"{r['budget_GiB']} GiB, n={r['n']}, {r['cache']}", r["step_ms"]
+        print(f"| {r['sweep']} | {pt} | {r['B']} | {ms} | {r['seq_steps_per_s']} | {r['GBs']} | {r['frac_8TBs']} |",
+              file=sys.stderr)
+
+
+# ---------------------------------------------------------------------------
 # rocprofv3 summaries -> profiles/
 # ---------------------------------------------------------------------------
 
@@ -378,6 +530,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["step", "copy"], default=None)
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
+    ap.add_argument("--sweeps", action="store_true")
     ap.add_argument("--command-note", default="")
     args = ap.parse_args()
     if args.summarize:
@@ -388,6 +541,9 @@ def main():
         print("bench.py measures one GPU only: the path shards by batch or kv head with no "
               "communication, and no multi-GPU figure is produced. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
+    if args.sweeps:
+        sweeps(args)
+        return
     run(args)
 
 
