@@ -121,8 +121,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ double s_c0[4];
   __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
-  __shared__ uint32_t s_adig[4][3][32];         // K-side A digits: [head][plane][128 channel bytes]
-  __shared__ uint32_t s_pdig[kWaves][4][3][32]; // V-side A digits per wave: [head][plane][128 token bytes]
+  __shared__ __align__(16) uint32_t s_adig[4][3][32];   // K-side A digits: [head][plane][128 channel bytes]
+  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][32];   // V-side A digits: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
@@ -505,6 +505,453 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   }
 }
 
+// b in {2, 4, 8}: the same two passes over b-bit codes.  A tile is 128/b
+// tokens, so that on either side a lane reads 8 words per tile:
+//   keys: lane (i16, g4) holds word planes b g4 .. b g4 + b - 1 (channels
+//     32 g4 .. +31, the A digits of the 1-bit kernel unchanged) of tokens
+//     TPL i16 .. +TPL-1, TPL = 8/b; a plane word spreads into byte-sized codes
+//     with one shift and mask per 4 codes;
+//   values: lane (i16, g4) holds V word row 4 tile + g4 (E = 32/b tokens) of
+//     channels 8 i16 .. +7; for b = 4 and 8 a lane's 16 contraction bytes are
+//     only half / a quarter used (the matrix cores have the headroom).
+// For b = 8 a code (0..255) is not a signed byte: it enters as its low nibble
+// plus twice (8 x high nibble), three products into the same accumulator.
+// The key dot product can exceed 32 bits for b >= 4 and is summed in 64 bits.
+template <int BITS, int G, bool F32>
+__global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
+  constexpr int E = 32 / BITS;                  // codes per word
+  constexpr int TB = 4 * E;                     // tokens per tile
+  constexpr int TPL = TB / 16;                  // key tokens per lane per tile
+  constexpr int W = 4 * BITS;                   // key word planes per token
+  constexpr uint32_t kNib = 0x0F0F0F0Fu;
+  const int unit = blockIdx.x;
+  const int b = unit / P.Hkv, h = unit % P.Hkv;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = P.n, T = P.T;
+  const int tiles = (n + TB - 1) / TB;
+  const int R = n / E;
+
+  __shared__ float s_q[4][128];
+  __shared__ float s_qp[4][128];
+  __shared__ double s_c0[4];
+  __shared__ float s_inv2f[4];
+  __shared__ int s_F[4];
+  __shared__ __align__(16) uint32_t s_adig[4][3][32];
+  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][TB / 4];   // V-side A digits: [head][plane][TB bytes]
+  __shared__ float s_ts[4][kMaxTail];
+  __shared__ float s_red[kWaves][4][2];
+  __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
+  __shared__ float s_tailred[kThreads / 128][4][128];
+  __shared__ float s_vred[kWaves][4][128];
+  __shared__ float s_psum[kWaves][4];
+
+  const int i16 = lane & 15, g4 = lane >> 4;
+  const int rh = i16 >> 2, rp = i16 & 3;
+  const int oh = lane >> 4;
+  const uint32_t* kc = P.kc;
+  auto load_k = [&](int tile, uint32_t (&w)[8]) {
+    const int tok0 = tile * TB + TPL * i16;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) w[q] = 0u;
+    if (tile < tiles && tok0 < n) {
+#pragma unroll
+      for (int p = 0; p < BITS; ++p) {
+        const uint32_t* src = kc + ((size_t)unit * W + BITS * g4 + p) * n + tok0;
+        if constexpr (TPL == 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(src);
+          w[4 * p] = x.x; w[4 * p + 1] = x.y; w[4 * p + 2] = x.z; w[4 * p + 3] = x.w;
+        } else if constexpr (TPL == 2) {
+          const uint2 x = *reinterpret_cast<const uint2*>(src);
+          w[2 * p] = x.x; w[2 * p + 1] = x.y;
+        } else {
+          w[p] = src[0];
+        }
+      }
+    }
+  };
+  uint32_t kn[8];
+  load_k(wave, kn);
+
+  // ---- prologue: post-scaled query, fixed-point digits -------------------
+  __shared__ double s_c0p[8];
+  __shared__ float s_mqp[8];
+  {                                             // thread: head tid / 128, channel tid % 128
+    const int hh = tid >> 7, j = tid & 127;
+    float qv = 0.f, qp = 0.f;
+    double pr = 0.0;
+    if (hh < G) {
+      qv = P.sm * ld_any(P.q, ((size_t)b * P.Hq + h * G + hh) * 128 + j, F32);
+      qp = qv * P.ks[(size_t)unit * 128 + j];
+      pr = (double)qv * (double)P.km[(size_t)unit * 128 + j];
+    }
+    s_q[hh][j] = qv;
+    s_qp[hh][j] = qp;
+    float aq = fabsf(qp);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      pr += __shfl_xor(pr, off);
+      aq = fmaxf(aq, __shfl_xor(aq, off));
+    }
+    if (lane == 0) {
+      s_c0p[wave] = pr;
+      s_mqp[wave] = aq;
+    }
+  }
+  __syncthreads();
+  if (tid < 4) {
+    const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
+    const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
+    int F = 0;
+    if (mq > 0.f) F = 21 - ilogbf(mq);
+    s_F[tid] = F;
+    s_inv2f[tid] = ldexpf(1.f, -F);
+    s_c0[tid] = c0;
+  }
+  __syncthreads();
+  {
+    const int hh = tid >> 7, j = tid & 127;
+    const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
+    const int d0 = ((Q + 128) & 255) - 128;
+    const int Q1 = (Q - d0) >> 8;
+    const int d1 = ((Q1 + 128) & 255) - 128;
+    const int d2 = (Q1 - d1) >> 8;
+    unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
+    ad[0 * 128 + j] = (unsigned char)d0;
+    ad[1 * 128 + j] = (unsigned char)d1;
+    ad[2 * 128 + j] = (unsigned char)d2;
+  }
+  __syncthreads();
+
+  // ---- pass 1: visual scores, their min and max --------------------------
+  v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
+  if (rp < 3 && rh < G) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
+    ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+    ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+  const float inv2f = s_inv2f[oh < G ? oh : 0];
+  const float c0f = (float)s_c0[oh < G ? oh : 0];
+  // score of key token m of this lane's TPL tokens (head oh)
+  auto score = [&](const uint32_t (&w)[8], int m) -> float {
+    v4i acc = {0, 0, 0, 0};
+    if constexpr (BITS == 2) {
+      const uint32_t w0 = w[m], w1 = w[TPL + m];
+      acc = mfma(ak0, v4i{(int)(w0 & 0x03030303u), (int)((w0 >> 2) & 0x03030303u), (int)((w0 >> 4) & 0x03030303u),
+                          (int)((w0 >> 6) & 0x03030303u)}, acc);
+      acc = mfma(ak1, v4i{(int)(w1 & 0x03030303u), (int)((w1 >> 2) & 0x03030303u), (int)((w1 >> 4) & 0x03030303u),
+                          (int)((w1 >> 6) & 0x03030303u)}, acc);
+    } else if constexpr (BITS == 4) {
+      const uint32_t w0 = w[m], w1 = w[TPL + m], w2 = w[2 * TPL + m], w3 = w[3 * TPL + m];
+      acc = mfma(ak0, v4i{(int)(w0 & kNib), (int)((w0 >> 4) & kNib), (int)(w1 & kNib), (int)((w1 >> 4) & kNib)}, acc);
+      acc = mfma(ak1, v4i{(int)(w2 & kNib), (int)((w2 >> 4) & kNib), (int)(w3 & kNib), (int)((w3 >> 4) & kNib)}, acc);
+    } else {
+      const v4i lo0{(int)(w[0] & kNib), (int)(w[1] & kNib), (int)(w[2] & kNib), (int)(w[3] & kNib)};
+      const v4i hi0{(int)((w[0] >> 1) & 0x78787878u), (int)((w[1] >> 1) & 0x78787878u),
+                    (int)((w[2] >> 1) & 0x78787878u), (int)((w[3] >> 1) & 0x78787878u)};
+      const v4i lo1{(int)(w[4] & kNib), (int)(w[5] & kNib), (int)(w[6] & kNib), (int)(w[7] & kNib)};
+      const v4i hi1{(int)((w[4] >> 1) & 0x78787878u), (int)((w[5] >> 1) & 0x78787878u),
+                    (int)((w[6] >> 1) & 0x78787878u), (int)((w[7] >> 1) & 0x78787878u)};
+      acc = mfma(ak0, lo0, acc);
+      acc = mfma(ak0, hi0, acc);
+      acc = mfma(ak0, hi0, acc);
+      acc = mfma(ak1, lo1, acc);
+      acc = mfma(ak1, hi1, acc);
+      acc = mfma(ak1, hi1, acc);
+    }
+    const long long dot = (long long)acc[0] + 256LL * acc[1] + 65536LL * acc[2];
+    float s = fmaf((float)dot, inv2f, c0f);
+    asm volatile("" : "+v"(s));
+    return s;
+  };
+  float vmin = INFINITY, vmax = -INFINITY;
+  for (int tile = wave; tile < tiles; tile += kWaves) {
+    uint32_t kw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) kw[q] = kn[q];
+    load_k(tile + kWaves, kn);
+    // n % 32 == 0: this lane's TPL tokens are all valid or none
+    const bool ok = tile * TB + TPL * i16 < n;
+#pragma unroll
+    for (int m = 0; m < TPL; ++m) {
+      const float s = score(kw, m);
+      if (ok) {
+        vmin = fminf(vmin, s);
+        vmax = fmaxf(vmax, s);
+      }
+    }
+  }
+  // second pass: first key and value tiles requested now (the key base goes
+  // through an opaque copy so that the compiler re-reads instead of keeping
+  // first-pass values alive)
+  asm("" : "+s"(kc));
+  load_k(wave, kn);
+  auto load_v = [&](int tile, uint32_t (&w)[8]) {
+    const int row = tile * 4 + g4;
+    if (tile < tiles && row < R) {
+      const uint4* src = reinterpret_cast<const uint4*>(P.vc + ((size_t)unit * R + row) * 128 + 8 * i16);
+      const uint4 x0 = src[0], x1 = src[1];
+      w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+      w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+    } else {
+#pragma unroll
+      for (int q = 0; q < 8; ++q) w[q] = 0u;
+    }
+  };
+  uint32_t vn[8];
+  load_v(wave, vn);
+  // ... and so are the first kPreTail tail tokens: keys as (token
+  // 4 wave + lane/16 + 32 r, channels 8 (lane%16) ..+7), values as (channel
+  // tid%128, tokens tid/128 + 4i).
+  const int tsub = lane >> 4, tcl = lane & 15;
+  constexpr int kKtRounds = kPreTail / (4 * kWaves);
+  uint4 ktp[kKtRounds][2];
+#pragma unroll
+  for (int r = 0; r < kKtRounds; ++r) {
+    const int j = 4 * wave + tsub + 4 * kWaves * r;
+    ktp[r][0] = make_uint4(0, 0, 0, 0);
+    ktp[r][1] = make_uint4(0, 0, 0, 0);
+    if (j < T) {
+      if constexpr (F32) {
+        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(P.kt) +
+                                                          ((size_t)unit * T + j) * 128 + 8 * tcl);
+        ktp[r][0] = src[0];
+        ktp[r][1] = src[1];
+      } else {
+        ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
+                                                    ((size_t)unit * T + j) * 128 + 8 * tcl);
+      }
+    }
+  }
+  constexpr int kPhases = kThreads / 128;
+  const int vtj = tid & 127, vtq = tid >> 7;
+  float vtp[kPreTail / kPhases];
+#pragma unroll
+  for (int i = 0; i < kPreTail / kPhases; ++i) {
+    const int t = vtq + kPhases * i;
+    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32) : 0.f;
+  }
+  // ---- text tail scores ---------------------------------------------------
+  {
+    const int sub = tsub, cl = tcl;
+#pragma unroll
+    for (int r = 0; r < kMaxTail / (4 * kWaves); ++r) {
+      const int j0 = 4 * wave + 4 * kWaves * r;
+      if (j0 >= T) break;
+      const int j = j0 + sub;
+      float kf[8];
+      if (r < kKtRounds) {                      // requested above
+        const uint4 ktp0 = ktp[r < kKtRounds ? r : 0][0], ktp1 = ktp[r < kKtRounds ? r : 0][1];
+        if constexpr (F32) {
+          kf[0] = __uint_as_float(ktp0.x); kf[1] = __uint_as_float(ktp0.y);
+          kf[2] = __uint_as_float(ktp0.z); kf[3] = __uint_as_float(ktp0.w);
+          kf[4] = __uint_as_float(ktp1.x); kf[5] = __uint_as_float(ktp1.y);
+          kf[6] = __uint_as_float(ktp1.z); kf[7] = __uint_as_float(ktp1.w);
+        } else {
+          const uint32_t hw[4] = {ktp0.x, ktp0.y, ktp0.z, ktp0.w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+          }
+        }
+      } else {
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float s = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
+        s += __shfl_xor(s, 8);
+        s += __shfl_xor(s, 4);
+        s += __shfl_xor(s, 2);
+        s += __shfl_xor(s, 1);
+        if (cl == 0 && j < T) s_ts[hh][j] = s;
+      }
+    }
+  }
+  // ---- min / max of every head's visual scores ---------------------------
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) {
+    vmin = fminf(vmin, __shfl_xor(vmin, off));
+    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
+  }
+  if ((lane & 15) == 0) {
+    s_red[wave][oh][0] = vmin;
+    s_red[wave][oh][1] = vmax;
+  }
+  __syncthreads();
+  if (wave < G) {                               // wave hh settles head hh
+    const int hh = wave;
+    float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
+    float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
+    float tmax = -INFINITY;
+    for (int j = lane; j < T; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) {
+      m = fminf(m, __shfl_xor(m, off));
+      M = fmaxf(M, __shfl_xor(M, off));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, off));
+    }
+    float lam = 1.f, mu = 0.f, vis_max = M;
+    if (P.calib_on && n > 0) {
+      const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
+      lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
+      mu = t_lo - lam * m;
+      vis_max = fmaxf(t_lo, t_hi);
+    }
+    const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
+    if (lane == 0) {
+      s_lam[hh] = lam * kLog2e;                 // p = 2^(s * lam' + mu')
+      s_mu[hh] = (mu - top) * kLog2e;
+    }
+    // tail probabilities (in place) and their sum
+    float pt = 0.f;
+    for (int j = lane; j < T; j += 64) {
+      const float pj = exp2f((s_ts[hh][j] - top) * kLog2e);
+      s_ts[hh][j] = pj;
+      pt += pj;
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
+    if (lane == 0) s_ptail[hh] = pt;
+  }
+  __syncthreads();
+  // text-tail values: thread (channel vtj, phase vtq) sums the tail tokens
+  // vtq + kPhases i for every head, the first kPreTail from the loads above
+  {
+    float ta[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < kPreTail / kPhases; ++i) {
+      const int t = vtq + kPhases * i;
+      if (t < T) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], vtp[i], ta[hh]);
+      }
+    }
+    for (int t = kPreTail + vtq; t < T; t += kPhases) {
+      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], v, ta[hh]);
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) s_tailred[vtq][hh][vtj] = ta[hh];
+  }
+
+  // ---- pass 2: values ------------------------------------------------------
+  const float lam2 = s_lam[oh < G ? oh : 0], mu2 = s_mu[oh < G ? oh : 0];
+  v4i vacc[8];
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
+  float psum = 0.f;
+  unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
+  for (int tile = wave; tile < tiles; tile += kWaves) {
+    uint32_t kw[8], vw[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) {
+      kw[q] = kn[q];
+      vw[q] = vn[q];
+    }
+    // (b = 8: the next key tile is requested once this one's scores are done,
+    // which keeps both key tiles from being live at once)
+    if constexpr (BITS < 8) load_k(tile + kWaves, kn);
+    load_v(tile + kWaves, vn);
+    const bool ok = oh < G && tile * TB + TPL * i16 < n;
+    uint32_t fb[TPL];
+#pragma unroll
+    for (int m = 0; m < TPL; ++m) {
+      const float s = score(kw, m);
+      float p = 0.f;
+      if (ok) p = exp2f(fmaf(s, lam2, mu2));
+      psum += p;
+      fb[m] = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) ^ 0x00008080u;   // bytes: P^0x80, (P>>8)^0x80, P>>16
+    }
+    if constexpr (BITS == 8) load_k(tile + kWaves, kn);
+    if (oh < G) {
+#pragma unroll
+      for (int pl = 0; pl < 3; ++pl) {
+        unsigned char* dst = pd + (oh * 3 + pl) * TB + TPL * i16;
+        if constexpr (TPL == 4) {
+          *reinterpret_cast<uint32_t*>(dst) = gather_byte(fb[0], fb[1], fb[2], fb[3], pl);
+        } else {
+#pragma unroll
+          for (int m = 0; m < TPL; ++m) dst[m] = (unsigned char)(fb[m] >> (8 * pl));
+        }
+      }
+    }
+    wave_sync_lds();
+    v4i av = {0, 0, 0, 0};
+    if (rp == 3) {
+      av = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
+    } else if (rh < G) {
+      const unsigned char* src = pd + (rh * 3 + rp) * TB + E * g4;
+      if constexpr (E == 16) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        av = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
+      } else if constexpr (E == 8) {
+        const uint2 x = *reinterpret_cast<const uint2*>(src);
+        av = v4i{(int)x.x, (int)x.y, 0, 0};
+      } else {
+        av = v4i{(int)*reinterpret_cast<const uint32_t*>(src), 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) {
+      const uint32_t w = vw[ct];
+      if constexpr (BITS == 2) {
+        vacc[ct] = mfma(av, v4i{(int)(w & 0x03030303u), (int)((w >> 2) & 0x03030303u),
+                                (int)((w >> 4) & 0x03030303u), (int)((w >> 6) & 0x03030303u)}, vacc[ct]);
+      } else if constexpr (BITS == 4) {
+        vacc[ct] = mfma(av, v4i{(int)(w & kNib), (int)((w >> 4) & kNib), 0, 0}, vacc[ct]);
+      } else {
+        const v4i lo{(int)(w & kNib), 0, 0, 0}, hi{(int)((w >> 1) & 0x78787878u), 0, 0, 0};
+        vacc[ct] = mfma(av, lo, vacc[ct]);
+        vacc[ct] = mfma(av, hi, vacc[ct]);
+        vacc[ct] = mfma(av, hi, vacc[ct]);
+      }
+    }
+    wave_sync_lds();                       // digits read before the next tile overwrites them
+  }
+
+  // ---- combine planes, reduce over waves --------------------------------
+  // lane (head oh, column i16): channels 8*i16 + ct
+#pragma unroll
+  for (int ct = 0; ct < 8; ++ct) {
+    const float cnt128 = 128.f * (float)vacc[ct][3];
+    const float sv = ((float)vacc[ct][0] + cnt128) + 256.f * ((float)vacc[ct][1] + cnt128) +
+                     65536.f * (float)vacc[ct][2];
+    s_vred[wave][oh][8 * i16 + ct] = sv * (1.f / 4194304.f);
+  }
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
+  if ((lane & 15) == 0) s_psum[wave][oh] = psum;
+  __syncthreads();
+  if (tid < G * 128) {
+    const int hh = tid >> 7, j = tid & 127;
+    float sv = 0.f, pv = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      sv += s_vred[w][hh][j];
+      pv += s_psum[w][hh];
+    }
+    float tail = 0.f;
+#pragma unroll
+    for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
+    const float pt = s_ptail[hh];
+    float o = tail;
+    if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
+    o /= (pv + pt);
+    const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
+    if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
+    else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);
+  }
+}
+
+
+
 template <int G, bool F32>
 hipError_t launch_g(const Params& p, int maxt, int units, hipStream_t st) {
   switch (maxt) {
@@ -522,6 +969,21 @@ hipError_t launch_f(const Params& p, int G, int maxt, int units, hipStream_t st)
   return launch_g<4, F32>(p, maxt, units, st);
 }
 
+template <int BITS, bool F32>
+hipError_t launch_bn(const Params& p, int G, int units, hipStream_t st) {
+  if (G == 1) { CQ_LAUNCH((df_bn<BITS, 1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_bn<BITS, 2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_bn<BITS, 4, F32>), dim3(units), dim3(kThreads), 0, st, p);
+  return hipSuccess;
+}
+
+template <bool F32>
+hipError_t launch_b(const Params& p, int bits, int G, int units, hipStream_t st) {
+  if (bits == 2) return launch_bn<2, F32>(p, G, units, st);
+  if (bits == 4) return launch_bn<4, F32>(p, G, units, st);
+  return launch_bn<8, F32>(p, G, units, st);
+}
+
 }  // namespace
 
 namespace cqi {
@@ -531,8 +993,9 @@ size_t decode_fast_ws(int, int, int, int, int, int) { return 0; }
 bool decode_fast_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
   const int tiles = (a.n + kTile - 1) / kTile;
-  return a.bits == 1 && a.d == 128 && (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 &&
-         tiles <= 8 * kWaves && a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
+  return (a.bits == 1 || a.bits == 2 || a.bits == 4 || a.bits == 8) && a.d == 128 &&
+         (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && (a.bits > 1 || tiles <= 8 * kWaves) &&
+         a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
 }
 
 hipError_t decode_fast(const DecodeArgs& a) {
@@ -544,6 +1007,9 @@ hipError_t decode_fast(const DecodeArgs& a) {
   const int tiles = (a.n + kTile - 1) / kTile;
   const int maxt = tiles <= kWaves ? 1 : (tiles <= 2 * kWaves ? 2 : (tiles <= 4 * kWaves ? 4 : 8));
   const int G = a.Hq / a.Hkv;
+  if (a.bits > 1)
+    return a.q_dtype == CQ_F32 ? launch_b<true>(p, a.bits, G, units, a.stream)
+                               : launch_b<false>(p, a.bits, G, units, a.stream);
   return a.q_dtype == CQ_F32 ? launch_f<true>(p, G, maxt, units, a.stream)
                              : launch_f<false>(p, G, maxt, units, a.stream);
 }

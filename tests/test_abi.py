@@ -82,7 +82,7 @@ def _decode(**kw):
     (dict(ws=None, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
-    (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), bits=2), 2),     # matrix-core path is 1-bit only
+    (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status

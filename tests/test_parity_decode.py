@@ -18,10 +18,10 @@ PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST]
 
 
 def fast_ok(q, K, kt, bits):
-    """Shapes the matrix-core decode kernel takes (else CQ_ERR_UNSUPPORTED)."""
+    """Shapes the matrix-core decode kernels take (else CQ_ERR_UNSUPPORTED)."""
     n, G = K.shape[2], q.shape[1] // K.shape[1]
     T = 0 if kt is None else kt.shape[2]
-    return (bits == 1 and G in (1, 2, 4) and n % 32 == 0 and -(-n // 128) <= 64 and T <= 256
+    return (G in (1, 2, 4) and n % 32 == 0 and (bits > 1 or -(-n // 128) <= 64) and T <= 256
             and (T == 0 or kt.dtype == q.dtype))
 
 
@@ -193,3 +193,23 @@ def test_fast_kernel_tile_counts(n, G):
     note(f"decode fast n={n} G={G}")
     got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST)
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), G)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("G", [1, 2, 4])
+@pytest.mark.parametrize("n", [32, 96, 1056, 3328])
+def test_fast_kernel_multibit(bits, G, n):
+    """Matrix-core kernels for b = 2, 4, 8: tiles of 128/b tokens, half-filled last tiles, tail."""
+    K, V, q, kt, vt = draw_inputs(1, 2 * G, 2, n, 64, seed=bits * 1000 + n + G)
+    note(f"decode fast bits={bits} n={n} G={G}")
+    got = _run(K, V, q, kt, vt, bits, None, cqb.CQ_PATH_FAST)
+    _compare(got, _oracle(K, V, q, kt, vt, bits, None), G)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+def test_fast_kernel_multibit_fp32_and_calibrated(bits):
+    import torch
+    K, V, q, kt, vt = draw_inputs(1, 8, 2, 320, 8, dtype="float32", seed=77 + bits)
+    note(f"decode fast bits={bits} fp32 calibrated")
+    got = _run(K, V, q, kt, vt, bits, RELATIVE, cqb.CQ_PATH_FAST, out_dtype=torch.float32)
+    _compare(got, _oracle(K, V, q, kt, vt, bits, RELATIVE), 4)
