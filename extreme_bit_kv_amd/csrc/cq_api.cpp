@@ -13,6 +13,9 @@ namespace {
 
 bool valid_bits(int32_t b) { return b == 1 || b == 2 || b == 4 || b == 8; }
 bool valid_dtype(int32_t t) { return t == CQ_F16 || t == CQ_F32; }
+// bulk buffers are read and written with 16-byte vector accesses
+bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 int opt_path(const cq_opts* o) { return o ? o->path : CQ_PATH_AUTO; }
 
 thread_local int32_t g_last_hip_error = 0;
@@ -77,6 +80,7 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
   if (units > 0) {
     if (scale == nullptr || minv == nullptr) return CQ_ERR_INVALID_ARG;
     if (n > 0 && (x == nullptr || codes == nullptr)) return CQ_ERR_INVALID_ARG;
+    if (!al16(x) || !al16(codes) || !al4(scale) || !al4(minv) || !al16(workspace)) return CQ_ERR_INVALID_ARG;
   }
   if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
   cqi::QuantArgs a{x, x_dtype, B, H, n, d, bits, layout, codes, scale, minv, workspace, (hipStream_t)stream};
@@ -119,6 +123,9 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
                   v_scale == nullptr || v_min == nullptr))
       return CQ_ERR_INVALID_ARG;
     if (T > 0 && (k_tail == nullptr || v_tail == nullptr)) return CQ_ERR_INVALID_ARG;
+    if (!al16(k_codes) || !al16(v_codes) || !al16(k_tail) || !al16(v_tail) || !al16(workspace) ||
+        !al4(k_scale) || !al4(k_min) || !al4(v_scale) || !al4(v_min) || !al4(q) || !al4(out))
+      return CQ_ERR_INVALID_ARG;
   }
   if (T == 0 && (k_tail != nullptr || v_tail != nullptr)) return CQ_ERR_INVALID_ARG;
   if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
@@ -169,6 +176,7 @@ cq_status cq_decode_attn_fp16(const void* q, const void* k, const void* v, int32
   if (!fits(B, Hkv, N, d) || !fits(B, Hq, 1, d) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || N < 1 || d <= 0)
     return CQ_ERR_INVALID_ARG;
   if (B > 0 && (q == nullptr || k == nullptr || v == nullptr || out == nullptr)) return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (!al16(k) || !al16(v) || !al16(workspace) || !al4(q) || !al4(out))) return CQ_ERR_INVALID_ARG;
   if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
   if (Hq / Hkv > 8) return CQ_ERR_UNSUPPORTED;
   const size_t need = cqi::decode_fp16_ws(B, Hq, Hkv, N, d);

@@ -41,24 +41,31 @@ __device__ __forceinline__ int exact_sign3(double a, double b, double c) {
   return (top > 0.0) - (top < 0.0);
 }
 
+// The exact half-integer test of exact_code, kept out of line: inlined, the
+// compiler evaluates it for every element and selects, although it is needed
+// only near a half-integer.
+__device__ __noinline__ int exact_tie_code(float x, float mn, float mx, int k, int L) {
+  k = k < 0 ? 0 : (k > L - 1 ? L - 1 : k);
+  const int s = exact_sign3(2.0 * L * (double)x, -(double)(2 * k + 1) * (double)mx,
+                            (double)(2 * k + 1 - 2 * L) * (double)mn);
+  return k + ((s > 0) || (s == 0 && (k & 1)));
+}
+
 // Round-half-to-even code of (x - mn) * L / (mx - mn), decided exactly.
-// `t` is an estimate of that quotient whose absolute error is far below
-// 2^-8; when it is not close to a half-integer the nearest integer is already
-// certain, otherwise the half-integer threshold k + 1/2 is tested exactly via
-// sign(2L*x - (2k+1)*mx + (2k+1-2L)*mn); each product is exact in float64
-// because x, mn, mx are float32-representable and the factors are < 2^10.
-__device__ __forceinline__ int exact_code(float x, float mn, float mx, double t, int L) {
-  double fl = floor(t);
-  double fr = t - fl;
+// `t` is an estimate of that quotient whose absolute error is below `window`
+// (by a safe margin); when it is farther than `window` from a half-integer
+// the nearest integer is already certain, otherwise the half-integer
+// threshold k + 1/2 is tested exactly via sign(2L*x - (2k+1)*mx +
+// (2k+1-2L)*mn); each product is exact in float64 because x, mn, mx are
+// float32-representable and the factors are < 2^10.
+__device__ __forceinline__ int exact_code(float x, float mn, float mx, double t, int L,
+                                          double window = 0.0078125) {
+  const double fl = floor(t);
   int c;
-  if (fabs(fr - 0.5) > 0.0078125) {
+  if (fabs((t - fl) - 0.5) > window) {
     c = (int)rint(t);
   } else {
-    int k = (int)fl;
-    k = k < 0 ? 0 : (k > L - 1 ? L - 1 : k);
-    int s = exact_sign3(2.0 * L * (double)x, -(double)(2 * k + 1) * (double)mx,
-                        (double)(2 * k + 1 - 2 * L) * (double)mn);
-    c = k + ((s > 0) || (s == 0 && (k & 1)));
+    c = exact_tie_code(x, mn, mx, (int)fl, L);
   }
   return c < 0 ? 0 : (c > L ? L : c);
 }

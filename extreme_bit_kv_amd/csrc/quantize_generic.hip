@@ -9,7 +9,7 @@
 // reduction of the chunks into min, max, the stored float32 scale and the
 // quotient estimate used for rounding, (3) code decision and packing.  The
 // input is read twice; the fused single-read kernel (quantize_fused.hip)
-// replaces this path for float16 inputs where it applies.
+// replaces this path for 1-bit float16 inputs.  Head dimension 128.
 #include "cq_device.h"
 #include "cq_internal.h"
 
@@ -17,35 +17,85 @@ namespace {
 
 constexpr int kChunk = 512;      // tokens per stats block
 constexpr int kThreads = 256;
+constexpr int kD = 128;          // head dimension (the only one the library takes)
 
 struct QParams {                 // per (unit, channel), in the workspace
   float mn, mx;
   double inv;                    // L / (mx - mn), 0 for a constant channel
 };
 
+// Values of 16 bytes of row data (8 float16 or 4 float32).
 template <typename T>
-__global__ void __launch_bounds__(kThreads) qz_stats(const T* __restrict__ x, int n, int d,
-                                                     int chunks, float2* __restrict__ part) {
-  const int unit = blockIdx.y, chunk = blockIdx.x;
-  const T* xu = x + (size_t)unit * n * d;
-  const int c = threadIdx.x % d, r0 = threadIdx.x / d, rs = kThreads / d;
-  const int i0 = chunk * kChunk, i1 = min(n, i0 + kChunk);
-  float lo = INFINITY, hi = -INFINITY;
-  for (int i = i0 + r0; i < i1; i += rs) {
-    float v = cqd::to_f32(xu[(size_t)i * d + c]);
-    lo = fminf(lo, v);
-    hi = fmaxf(hi, v);
-  }
-  __shared__ float slo[kThreads], shi[kThreads];
-  slo[threadIdx.x] = lo;
-  shi[threadIdx.x] = hi;
-  __syncthreads();
-  if (r0 == 0) {
-    for (int r = 1; r < rs; ++r) {
-      lo = fminf(lo, slo[r * d + c]);
-      hi = fmaxf(hi, shi[r * d + c]);
+__device__ __forceinline__ void unpack16(const uint4& raw, float* v) {
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  if constexpr (sizeof(T) == 2) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __half2float(__ushort_as_half((unsigned short)(w[k] & 0xFFFFu)));
+      v[2 * k + 1] = __half2float(__ushort_as_half((unsigned short)(w[k] >> 16)));
     }
-    part[((size_t)unit * chunks + chunk) * d + c] = make_float2(lo, hi);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) v[k] = __uint_as_float(w[k]);
+  }
+}
+
+// N consecutive values from p (16-byte vector loads; 8-byte ones for four float16).
+template <typename T, int N>
+__device__ __forceinline__ void load_vals(const T* p, float (&v)[N]) {
+  constexpr int kPer = 16 / (int)sizeof(T);
+  if constexpr (N >= kPer) {
+#pragma unroll
+    for (int k = 0; k < N / kPer; ++k) unpack16<T>(reinterpret_cast<const uint4*>(p)[k], v + k * kPer);
+  } else {
+    static_assert(sizeof(T) == 2 && N == 4, "four float16 values");
+    const uint2 raw = *reinterpret_cast<const uint2*>(p);
+    v[0] = __half2float(__ushort_as_half((unsigned short)(raw.x & 0xFFFFu)));
+    v[1] = __half2float(__ushort_as_half((unsigned short)(raw.x >> 16)));
+    v[2] = __half2float(__ushort_as_half((unsigned short)(raw.y & 0xFFFFu)));
+    v[3] = __half2float(__ushort_as_half((unsigned short)(raw.y >> 16)));
+  }
+}
+
+// Per-(unit, chunk) channel min/max: a thread reads 16 bytes of a row
+// (channels kVec cg .. +kVec-1), kRows rows of the chunk at a time.
+template <typename T>
+__global__ void __launch_bounds__(kThreads) qz_stats(const T* __restrict__ x, int n, int chunks,
+                                                     float2* __restrict__ part) {
+  constexpr int kVec = 16 / (int)sizeof(T), kTpr = kD / kVec, kRows = kThreads / kTpr;
+  const int unit = blockIdx.y, chunk = blockIdx.x;
+  const T* xu = x + (size_t)unit * n * kD;
+  const int cg = threadIdx.x % kTpr, r0 = threadIdx.x / kTpr;
+  const int i0 = chunk * kChunk, i1 = min(n, i0 + kChunk);
+  float lo[kVec], hi[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) { lo[e] = INFINITY; hi[e] = -INFINITY; }
+#pragma unroll 4
+  for (int i = i0 + r0; i < i1; i += kRows) {
+    float v[kVec];
+    load_vals<T, kVec>(xu + (size_t)i * kD + cg * kVec, v);
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) {
+      lo[e] = fminf(lo[e], v[e]);
+      hi[e] = fmaxf(hi[e], v[e]);
+    }
+  }
+  __shared__ float slo[kRows][kD], shi[kRows][kD];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) {
+    slo[r0][cg * kVec + e] = lo[e];
+    shi[r0][cg * kVec + e] = hi[e];
+  }
+  __syncthreads();
+  if (threadIdx.x < kD) {
+    const int c = threadIdx.x;
+    float l = INFINITY, h = -INFINITY;
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+      l = fminf(l, slo[r][c]);
+      h = fmaxf(h, shi[r][c]);
+    }
+    part[((size_t)unit * chunks + chunk) * kD + c] = make_float2(l, h);
   }
 }
 
@@ -96,49 +146,79 @@ __global__ void qz_params(const float2* __restrict__ part, int chunks, int d, in
   prm[(size_t)unit * d + c] = p;
 }
 
-template <typename T>
-__device__ __forceinline__ int code_of(T xv, const QParams& p, int L) {
+// The float64 estimate t of (x - mn) L / (mx - mn) is off the exact quotient
+// by at most 3 * 2^-53 * L < 2^-43 (x - mn is exact in float64 for
+// float32-representable operands; inv and the product are one rounding each),
+// so the exact test is needed only within 2^-30 of a half-integer: in
+// practice for exact ties alone, and whole wavefronts seldom take it.
+__device__ __forceinline__ int code_of(float x, const QParams& p, int L) {
   if (!(p.inv > 0.0)) return 0;
-  float x = cqd::to_f32(xv);
-  double t = ((double)x - (double)p.mn) * p.inv;
-  return cqd::exact_code(x, p.mn, p.mx, t, L);
+  const double t = ((double)x - (double)p.mn) * p.inv;
+  return cqd::exact_code(x, p.mn, p.mx, t, L, 0x1p-30);
 }
 
-// K layout: one thread per word (w, i).
-template <typename T>
-__global__ void __launch_bounds__(kThreads) qz_pack_k(const T* __restrict__ x, int n, int d, int bits,
+// K layout: a block packs kTok tokens.  Words are computed with the word
+// index fastest across threads (a wave reads whole rows), staged in LDS, and
+// written plane by plane (kTok consecutive words of a plane per wave).
+constexpr int kTok = 64;
+template <typename T, int BITS>
+__global__ void __launch_bounds__(kThreads) qz_pack_k(const T* __restrict__ x, int n,
                                                       const QParams* __restrict__ prm,
                                                       uint32_t* __restrict__ codes) {
-  const int unit = blockIdx.y;
-  const int E = 32 / bits, W = d / E, L = (1 << bits) - 1;
-  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (long)W * n) return;
-  const int w = (int)(idx / n), i = (int)(idx % n);
-  const T* row = x + ((size_t)unit * n + i) * d + w * E;
-  const QParams* pu = prm + (size_t)unit * d + w * E;
-  uint32_t word = 0;
-  for (int e = 0; e < E; ++e) word |= (uint32_t)code_of(row[e], pu[e], L) << cqd::code_off(e, bits);
-  codes[((size_t)unit * W + w) * n + i] = word;
-}
-
-// V layout: one thread per word (r, j).
-template <typename T>
-__global__ void __launch_bounds__(kThreads) qz_pack_v(const T* __restrict__ x, int n, int d, int bits,
-                                                      const QParams* __restrict__ prm,
-                                                      uint32_t* __restrict__ codes) {
-  const int unit = blockIdx.y;
-  const int E = 32 / bits, R = (n + E - 1) / E, L = (1 << bits) - 1;
-  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (long)R * d) return;
-  const int r = (int)(idx / d), j = (int)(idx % d);
-  const QParams p = prm[(size_t)unit * d + j];
-  const T* col = x + (size_t)unit * n * d + j;
-  uint32_t word = 0;
-  for (int e = 0; e < E; ++e) {
-    int i = r * E + e;
-    if (i < n) word |= (uint32_t)code_of(col[(size_t)i * d], p, L) << cqd::code_off(e, bits);
+  constexpr int E = 32 / BITS, W = kD / E, L = (1 << BITS) - 1;
+  const int unit = blockIdx.y, i0 = blockIdx.x * kTok;
+  __shared__ QParams sp[kD];                     // the unit's channel parameters
+  __shared__ uint32_t sw[W][kTok + 1];
+  if (threadIdx.x < kD) sp[threadIdx.x] = prm[(size_t)unit * kD + threadIdx.x];
+  __syncthreads();
+  for (int q = threadIdx.x; q < kTok * W; q += kThreads) {
+    const int w = q % W, ti = q / W, i = i0 + ti;
+    uint32_t word = 0;
+    if (i < n) {
+      float v[E];
+      load_vals<T, E>(x + ((size_t)unit * n + i) * kD + w * E, v);
+#pragma unroll
+      for (int e = 0; e < E; ++e) word |= (uint32_t)code_of(v[e], sp[w * E + e], L) << cqd::code_off(e, BITS);
+    }
+    sw[w][ti] = word;
   }
-  codes[((size_t)unit * R + r) * d + j] = word;
+  __syncthreads();
+  for (int q = threadIdx.x; q < kTok * W; q += kThreads) {
+    const int w = q / kTok, ti = q % kTok, i = i0 + ti;
+    if (i < n) codes[((size_t)unit * W + w) * n + i] = sw[w][ti];
+  }
+}
+
+// V layout: thread (r, cg) packs the words (r, 8 cg .. 8 cg + 7): per token of
+// the row it reads 16 bytes (8 channels) and stores two 16-byte word groups.
+template <typename T, int BITS>
+__global__ void __launch_bounds__(kThreads) qz_pack_v(const T* __restrict__ x, int n,
+                                                      const QParams* __restrict__ prm,
+                                                      uint32_t* __restrict__ codes) {
+  constexpr int E = 32 / BITS, L = (1 << BITS) - 1;
+  const int unit = blockIdx.y;
+  const int R = (n + E - 1) / E;
+  __shared__ QParams sp[kD];
+  if (threadIdx.x < kD) sp[threadIdx.x] = prm[(size_t)unit * kD + threadIdx.x];
+  __syncthreads();
+  const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
+  if (idx >= (long)R * (kD / 8)) return;
+  const int r = (int)(idx / (kD / 8)), cg = (int)(idx % (kD / 8));
+  const T* xu = x + (size_t)unit * n * kD + 8 * cg;
+  uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
+#pragma unroll 4
+  for (int e = 0; e < E; ++e) {
+    const int i = r * E + e;
+    if (i < n) {
+      float v[8];
+      load_vals<T, 8>(xu + (size_t)i * kD, v);
+#pragma unroll
+      for (int c = 0; c < 8; ++c) word[c] |= (uint32_t)code_of(v[c], sp[8 * cg + c], L) << cqd::code_off(e, BITS);
+    }
+  }
+  uint4* dst = reinterpret_cast<uint4*>(codes + ((size_t)unit * R + r) * kD + 8 * cg);
+  dst[0] = make_uint4(word[0], word[1], word[2], word[3]);
+  dst[1] = make_uint4(word[4], word[5], word[6], word[7]);
 }
 
 // Empty cache: scale = minv = 0.
@@ -148,6 +228,20 @@ __global__ void qz_zero(float* scale, float* minv, long count) {
     scale[i] = 0.0f;
     minv[i] = 0.0f;
   }
+}
+
+template <typename T, int BITS>
+hipError_t pack(const cqi::QuantArgs& a, const T* x, const QParams* prm, int units) {
+  constexpr int E = 32 / BITS;
+  if (a.layout == CQ_LAYOUT_K) {
+    CQ_LAUNCH((qz_pack_k<T, BITS>), dim3((unsigned)((a.n + kTok - 1) / kTok), units), dim3(kThreads), 0,
+              a.stream, x, a.n, prm, a.codes);
+  } else {
+    const long threads = (long)((a.n + E - 1) / E) * (kD / 8);
+    CQ_LAUNCH((qz_pack_v<T, BITS>), dim3((unsigned)((threads + kThreads - 1) / kThreads), units), dim3(kThreads),
+              0, a.stream, x, a.n, prm, a.codes);
+  }
+  return hipSuccess;
 }
 
 template <typename T>
@@ -164,20 +258,15 @@ hipError_t run(const cqi::QuantArgs& a) {
   float2* part = (float2*)a.ws;
   QParams* prm = (QParams*)((char*)a.ws + cqi::align_up((size_t)units * chunks * a.d * sizeof(float2), 256));
   const T* x = (const T*)a.x;
-  CQ_LAUNCH(qz_stats<T>, dim3(chunks, units), dim3(kThreads), 0, a.stream, x, a.n, a.d, chunks, part);
+  CQ_LAUNCH(qz_stats<T>, dim3(chunks, units), dim3(kThreads), 0, a.stream, x, a.n, chunks, part);
   CQ_LAUNCH(qz_params, dim3(units), dim3(a.d), 0, a.stream, part, chunks, a.d, a.bits, a.scale, a.minv,
                      prm);
-  const int E = 32 / a.bits;
-  if (a.layout == CQ_LAYOUT_K) {
-    long words = (long)(a.d / E) * a.n;
-    CQ_LAUNCH(qz_pack_k<T>, dim3((unsigned)((words + kThreads - 1) / kThreads), units), dim3(kThreads), 0,
-                       a.stream, x, a.n, a.d, a.bits, prm, a.codes);
-  } else {
-    long words = (long)((a.n + E - 1) / E) * a.d;
-    CQ_LAUNCH(qz_pack_v<T>, dim3((unsigned)((words + kThreads - 1) / kThreads), units), dim3(kThreads), 0,
-                       a.stream, x, a.n, a.d, a.bits, prm, a.codes);
+  switch (a.bits) {
+    case 1: return pack<T, 1>(a, x, prm, units);
+    case 2: return pack<T, 2>(a, x, prm, units);
+    case 4: return pack<T, 4>(a, x, prm, units);
+    default: return pack<T, 8>(a, x, prm, units);
   }
-  return hipSuccess;
 }
 
 }  // namespace

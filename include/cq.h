@@ -28,6 +28,10 @@
  *     CQ_ERR_HIP means a HIP launch call failed (work enqueued before the
  *     failing launch may still run).  Faults inside kernels surface at the
  *     caller's next synchronization, as for any HIP kernel.
+ *   - Alignment: bulk device buffers (x, code words, tails, the fp16
+ *     baseline's k and v, workspaces) must be 16-byte aligned, every other
+ *     device pointer 4-byte aligned (torch allocations are 256-byte
+ *     aligned); CQ_ERR_INVALID_ARG otherwise.
  *   - No C++ exception crosses the ABI.
  *
  * Packed code format (this library's storage format; the pages only say that

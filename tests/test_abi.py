@@ -13,6 +13,7 @@ cqb = pytest.importorskip("extreme_bit_kv_amd", reason="libcq.so not built")
 lib = cqb.lib
 
 FAKE = ctypes.c_void_p(0x10000)       # never dereferenced: every call below fails validation
+ODD = ctypes.c_void_p(0x10008)        # 8-byte aligned only: bulk buffers must be 16-byte aligned
 
 
 def _declared():
@@ -57,6 +58,7 @@ def _quant(**kw):
     (dict(B=-1), 1), (dict(d=48, bits=1), 1), (dict(d=64), 2), (dict(d=256), 2),
     (dict(ws=None), 3), (dict(wsb=16), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(9, 0))), 1),
+    (dict(x=ODD), 1), (dict(codes=ODD), 1), (dict(ws=ODD), 1), (dict(scale=ctypes.c_void_p(0x10002)), 1),
 ])
 def test_quantize_rejects(kw, status):
     assert _quant(**kw) == status
@@ -83,6 +85,7 @@ def _decode(**kw):
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
+    (dict(kc=ODD), 1), (dict(vc=ODD), 1), (dict(kt=ODD), 1), (dict(ws=ODD), 1), (dict(q=ctypes.c_void_p(0x10001)), 1),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
@@ -102,6 +105,7 @@ def test_fp16_baseline_rejects():
     assert f(FAKE, FAKE, FAKE, 1, 32, 8, 0, 128, 0.1, FAKE, FAKE, 1 << 30, None) == 1
     assert f(FAKE, FAKE, FAKE, 1, 32, 8, 64, 64, 0.1, FAKE, FAKE, 1 << 30, None) == 2
     assert f(FAKE, FAKE, FAKE, 1, 32, 8, 64, 128, 0.1, FAKE, None, 0, None) == 3
+    assert f(FAKE, ODD, FAKE, 1, 32, 8, 64, 128, 0.1, FAKE, FAKE, 1 << 30, None) == 1
 
 
 def test_empty_batch_is_a_no_op_without_gpu_work():
