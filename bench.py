@@ -52,6 +52,19 @@ PROFILES = os.path.join(ROOT, "profiles")
 # algorithmic byte counts
 # ---------------------------------------------------------------------------
 
+class Flush:
+    """Evicts the Infinity Cache before a cold measurement by reading 512 MiB
+    (twice its size).  A read, not a fill: a fill leaves the cache full of
+    dirty lines whose write-back then lands inside the timed kernel."""
+
+    def __init__(self, dev):
+        import torch
+        self.buf = torch.zeros(128 << 20, dtype=torch.float32, device=dev)
+
+    def __call__(self):
+        self.buf.sum()
+
+
 def quant_bytes(cfg):
     """One cq_quantize_kv launch over one of K or V: read fp16 x, write codes and 2 fp32 vectors."""
     units = cfg.B * cfg.Hkv
@@ -232,10 +245,10 @@ def run(args):
         return
 
     # decode alone with the Infinity Cache flushed before every call
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = Flush(dev)
     cold = []
     for _ in range(max(10, args.steps)):
-        scratch.zero_()
+        scratch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         decode()
@@ -252,7 +265,7 @@ def run(args):
                       dtype=torch.uint8, device=dev)
     fcold = []
     for _ in range(max(10, args.steps)):
-        scratch.zero_()
+        scratch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
         cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=of, workspace=fws)
@@ -333,7 +346,7 @@ def sweeps(args):
             fn()
         for _ in range(reps):
             if flush is not None:
-                flush.zero_()
+                flush()
             a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             a.record()
             fn()
@@ -347,7 +360,7 @@ def sweeps(args):
         print(json.dumps(row), flush=True)
 
     # -- bit-width sweep: one layer, B=32, n=3328, decode with the Infinity Cache flushed
-    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scratch = Flush(dev)
     base = CONFIGS["bits_sweep_b1"]
     K = kv_torch(base.seed, 0, ROLE_K, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
     V = kv_torch(base.seed, 0, ROLE_V, base.B, base.Hkv, base.n, base.d, base.dtype, dev)

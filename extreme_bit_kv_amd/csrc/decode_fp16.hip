@@ -1,201 +1,246 @@
 // Unquantized float16 split-K decode attention: the comparison baseline for
 // the 1-bit path (not part of the method).  Each block owns one token split
-// of one (batch, kv head): it computes the scores of its tokens for every
-// query head of the group into LDS, takes their max, and accumulates
-// p * V in float32; a second launch merges the split partials by
-// log-sum-exp.  A wave reads four 256-byte rows per load (16 lanes x 16 B),
-// so K and V stream through HBM once, fully coalesced.
+// of one (batch, kv head) and makes one pass over it with an online softmax
+// (flash-decoding): K and V rows are read together, so each byte crosses HBM
+// once.  A 16-lane group holds one 256-byte row (16 B per lane); a wave reads
+// four rows per load and keeps four loads of K and four of V in flight.
+// Scores use packed fp16 dot products with float32 accumulation; every
+// 16-lane group keeps its own running max, sum and float32 p*V accumulator,
+// and the groups and waves combine at the end.  A second launch merges the
+// split partials by log-sum-exp.
 #include "cq_device.h"
 #include "cq_internal.h"
 
+#include <algorithm>
+
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr int kGMax = 8;
 constexpr int kD = cqd::kD;
-constexpr int kMaxSplit = 1024;     // tokens per split (scores live in LDS)
-constexpr int kRec = kD + 2;        // [max, l, acc[d]]
+constexpr int kRows = 4;              // rows per 16-lane group per step
+constexpr int kStep = kWaves * 4 * kRows;   // rows per block per step
+constexpr int kRec = kD + 2;          // [max (log2 domain), l, acc[d]]
+constexpr int kSplitRows = 1024;     // rows per split when that gives enough blocks
+constexpr int kMinBlocks = 1024;     // two rounds of resident blocks (2 per CU)
+
+typedef _Float16 h2 __attribute__((ext_vector_type(2)));
 
 struct Shape {
   int B, Hq, Hkv, G, N, S, per;
 };
 
-__device__ __forceinline__ void load8(const __half* p, float* f) {
-  uint4 raw = *reinterpret_cast<const uint4*>(p);
-  const __half2* h = reinterpret_cast<const __half2*>(&raw);
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    float2 v = __half22float2(h[k]);
-    f[2 * k] = v.x;
-    f[2 * k + 1] = v.y;
-  }
+// x + x rotated by R lanes within its row of 16 lanes (DPP row_ror).
+template <int R>
+__device__ __forceinline__ float add_ror(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R,
+                                                                   0xF, 0xF, false));
 }
 
+// Sums over the 16 lanes of a row (every lane receives its row's sum): rotations
+// by 8, 4, 2 and 1 lanes, the independent sums interleaved so that each DPP
+// read is not right behind the write it depends on.
+template <int N>
+__device__ __forceinline__ void row_sum16(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = add_ror<8>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = add_ror<4>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = add_ror<2>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = add_ror<1>(x[i]);
+}
+
+__device__ __forceinline__ h2 as_h2(uint32_t w) { return __builtin_bit_cast(h2, w); }
+
+template <int G>
 __global__ void __launch_bounds__(kThreads) f16_split(Shape sh, const __half* __restrict__ q,
                                                       const __half* __restrict__ k,
-                                                      const __half* __restrict__ v, float sm,
+                                                      const __half* __restrict__ v, float sm_log2,
                                                       float* __restrict__ part) {
   const int unit = blockIdx.y, split = blockIdx.x;
-  const int b = unit / sh.Hkv, h = unit % sh.Hkv, G = sh.G;
+  const int b = unit / sh.Hkv, h = unit % sh.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int sub = lane >> 4, cl = lane & 15;          // token row within the wave load, channel chunk
+  const int sub = lane >> 4, cl = lane & 15;          // row within a 4-row load, 8-channel chunk
   const int t0 = min(sh.N, split * sh.per), t1 = min(sh.N, t0 + sh.per);
-  __shared__ float sc[kGMax][kMaxSplit];
-  __shared__ float red[kGMax][kWaves * 4];
-  __shared__ float accs[kWaves][kGMax][kD];
 
-  float qr[kGMax][8];
+  uint4 qw[G];
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
-    if (g < G) {
-      load8(q + ((size_t)b * sh.Hq + h * G + g) * kD + cl * 8, qr[g]);
-#pragma unroll
-      for (int c = 0; c < 8; ++c) qr[g][c] *= sm;
-    }
+  for (int g = 0; g < G; ++g) {   // q is only 4-byte aligned
+    const uint32_t* qp = reinterpret_cast<const uint32_t*>(q + ((size_t)b * sh.Hq + h * G + g) * kD + cl * 8);
+    qw[g] = make_uint4(qp[0], qp[1], qp[2], qp[3]);
   }
-  const __half* ku = k + (size_t)unit * sh.N * kD;
-  const __half* vu = v + (size_t)unit * sh.N * kD;
-  // ---- scores ------------------------------------------------------------
-  float mloc[kGMax];
+  const __half* ku = k + (size_t)unit * sh.N * kD + cl * 8;
+  const __half* vu = v + (size_t)unit * sh.N * kD + cl * 8;
+
+  float m[G], l[G], acc[G][8];
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) mloc[g] = -INFINITY;
-  for (int base = t0; base < t1; base += kWaves * 4) {
-    const int tok = base + wave * 4 + sub;
-    float kf[8];
-    if (tok < t1) load8(ku + (size_t)tok * kD + cl * 8, kf);
-    else {
-#pragma unroll
-      for (int c = 0; c < 8; ++c) kf[c] = 0.f;
-    }
-#pragma unroll
-    for (int g = 0; g < kGMax; ++g) {
-      if (g < G) {
-        float s = 0.f;
-#pragma unroll
-        for (int c = 0; c < 8; ++c) s = fmaf(qr[g][c], kf[c], s);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
-        if (tok < t1) {
-          if (cl == 0) sc[g][tok - t0] = s;
-          mloc[g] = fmaxf(mloc[g], s);
-        }
-      }
-    }
-  }
-  // block max per head
-  if (cl == 0) {
-#pragma unroll
-    for (int g = 0; g < kGMax; ++g)
-      if (g < G) red[g][wave * 4 + sub] = mloc[g];
-  }
-  __syncthreads();
-  __shared__ float smax[kGMax], ssum[kGMax];
-  if (threadIdx.x < G) {
-    float m = -INFINITY;
-    for (int k2 = 0; k2 < kWaves * 4; ++k2) m = fmaxf(m, red[threadIdx.x][k2]);
-    smax[threadIdx.x] = m;
-  }
-  __syncthreads();
-  // probabilities in place, and their sums
-  const int cnt = t1 - t0;
-  __shared__ float red2[kGMax][kWaves];
   for (int g = 0; g < G; ++g) {
-    float l = 0.f;
-    for (int i = threadIdx.x; i < cnt; i += kThreads) {
-      float p = __expf(sc[g][i] - smax[g]);
-      sc[g][i] = p;
-      l += p;
-    }
-    for (int off = 32; off > 0; off >>= 1) l += __shfl_xor(l, off);
-    if (lane == 0) red2[g][wave] = l;
-  }
-  __syncthreads();
-  if (threadIdx.x < G) {
-    float l = 0.f;
-    for (int w = 0; w < kWaves; ++w) l += red2[threadIdx.x][w];
-    ssum[threadIdx.x] = l;
-  }
-  // ---- values ------------------------------------------------------------
-  float acc[kGMax][8];
-#pragma unroll
-  for (int g = 0; g < kGMax; ++g)
+    m[g] = -INFINITY;
+    l[g] = 0.f;
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
-  for (int base = t0; base < t1; base += kWaves * 4) {
-    const int tok = base + wave * 4 + sub;
-    if (tok < t1) {
-      float vf[8];
-      load8(vu + (size_t)tok * kD + cl * 8, vf);
+  }
+  for (int base = t0 + wave * 4 * kRows; base < t1; base += kStep) {
+    // rows past the split re-read its last row (in bounds) and get p = 0
+    uint4 kr[kRows], vr[kRows];
 #pragma unroll
-      for (int g = 0; g < kGMax; ++g) {
-        if (g < G) {
-          float p = sc[g][tok - t0];
+    for (int r = 0; r < kRows; ++r)
+      kr[r] = *reinterpret_cast<const uint4*>(ku + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
 #pragma unroll
-          for (int c = 0; c < 8; ++c) acc[g][c] = fmaf(p, vf[c], acc[g][c]);
+    for (int r = 0; r < kRows; ++r)
+      vr[r] = *reinterpret_cast<const uint4*>(vu + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float s[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        float d = 0.f;
+        d = __builtin_amdgcn_fdot2(as_h2(qw[g].x), as_h2(kr[r].x), d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(qw[g].y), as_h2(kr[r].y), d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(qw[g].z), as_h2(kr[r].z), d, false);
+        d = __builtin_amdgcn_fdot2(as_h2(qw[g].w), as_h2(kr[r].w), d, false);
+        s[r] = d;
+      }
+      row_sum16(s);
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) s[r] = base + r * 4 + sub < t1 ? s[r] * sm_log2 : -INFINITY;
+      float mn = m[g];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) mn = fmaxf(mn, s[r]);
+      const float mu = mn == -INFINITY ? 0.f : mn;   // a fully masked group keeps p = alpha = 0
+      // v_exp_f32 directly: results below 2^-126 flush to 0, which a softmax weight can lose
+      const float alpha = __builtin_amdgcn_exp2f(m[g] - mu);
+      float p[kRows];
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) p[r] = __builtin_amdgcn_exp2f(s[r] - mu);
+      float ps = 0.f;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) ps += p[r];
+      l[g] = l[g] * alpha + ps;
+      m[g] = mn;
+#pragma unroll
+      for (int c = 0; c < 8; ++c) acc[g][c] *= alpha;
+#pragma unroll
+      for (int r = 0; r < kRows; ++r) {
+        const uint32_t w[4] = {vr[r].x, vr[r].y, vr[r].z, vr[r].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const h2 vv = as_h2(w[c]);
+          acc[g][2 * c] = fmaf(p[r], (float)vv.x, acc[g][2 * c]);
+          acc[g][2 * c + 1] = fmaf(p[r], (float)vv.y, acc[g][2 * c + 1]);
         }
       }
     }
   }
+  // combine the four row groups of the wave (lanes 16 and 32 apart)
 #pragma unroll
-  for (int g = 0; g < kGMax; ++g) {
-    if (g < G) {
+  for (int g = 0; g < G; ++g) {
+    float M = fmaxf(m[g], __shfl_xor(m[g], 16));
+    M = fmaxf(M, __shfl_xor(M, 32));
+    const float sc = M == -INFINITY ? 0.f : exp2f(m[g] - M);
+    l[g] *= sc;
+    l[g] += __shfl_xor(l[g], 16);
+    l[g] += __shfl_xor(l[g], 32);
 #pragma unroll
-      for (int c = 0; c < 8; ++c) {
-        float a = acc[g][c];
-        a += __shfl_xor(a, 16);
-        a += __shfl_xor(a, 32);
-        if (sub == 0) accs[wave][g][cl * 8 + c] = a;
+    for (int c = 0; c < 8; ++c) {
+      float a = acc[g][c] * sc;
+      a += __shfl_xor(a, 16);
+      a += __shfl_xor(a, 32);
+      acc[g][c] = a;
+    }
+    m[g] = M;
+  }
+  // combine the waves
+  __shared__ float s_acc[kWaves][G][kD];
+  __shared__ float s_ml[kWaves][G][2];
+  if (sub == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) s_acc[wave][g][cl * 8 + c] = acc[g][c];
+      if (cl == 0) {
+        s_ml[wave][g][0] = m[g];
+        s_ml[wave][g][1] = l[g];
       }
     }
   }
   __syncthreads();
   float* rec = part + ((size_t)unit * sh.S + split) * G * kRec;
   for (int idx = threadIdx.x; idx < G * kD; idx += kThreads) {
-    int g = idx / kD, j = idx % kD;
-    float a = 0.f;
+    const int g = idx / kD, j = idx % kD;
+    float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) a += accs[w][g][j];
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_ml[w][g][0]);
+    float a = 0.f, ls = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float sc = s_ml[w][g][0] == -INFINITY ? 0.f : exp2f(s_ml[w][g][0] - M);
+      a = fmaf(sc, s_acc[w][g][j], a);
+      ls = fmaf(sc, s_ml[w][g][1], ls);
+    }
     rec[g * kRec + 2 + j] = a;
-  }
-  if (threadIdx.x < G) {
-    rec[threadIdx.x * kRec + 0] = smax[threadIdx.x];
-    rec[threadIdx.x * kRec + 1] = cnt > 0 ? ssum[threadIdx.x] : 0.f;
+    if (j == 0) {
+      rec[g * kRec + 0] = M;
+      rec[g * kRec + 1] = ls;
+    }
   }
 }
 
-__global__ void f16_merge(Shape sh, const float* __restrict__ part, __half* __restrict__ out) {
+// One block of kD threads per (batch, query head).  Each wave forms the
+// log-sum-exp weights of the S split partials itself (lanes over splits),
+// then thread j sums weight * acc[j] over the splits.
+__global__ void __launch_bounds__(kD) f16_merge(Shape sh, const float* __restrict__ part,
+                                                __half* __restrict__ out) {
   const int hq_all = blockIdx.x;
   const int b = hq_all / sh.Hq, hq = hq_all % sh.Hq, h = hq / sh.G, g = hq % sh.G;
-  const int unit = b * sh.Hkv + h, j = threadIdx.x;
-  const float* base = part + (size_t)unit * sh.S * sh.G * kRec;
-  float Mx = -INFINITY;
-  for (int s = 0; s < sh.S; ++s) {
-    const float* rec = base + ((size_t)s * sh.G + g) * kRec;
-    if (rec[1] > 0.f) Mx = fmaxf(Mx, rec[0]);
+  const int unit = b * sh.Hkv + h, j = threadIdx.x, lane = threadIdx.x & 63;
+  const float* base = part + (size_t)unit * sh.S * sh.G * kRec + (size_t)g * kRec;
+  const size_t stride = (size_t)sh.G * kRec;   // between splits
+  float mx = -INFINITY;
+  for (int s = lane; s < sh.S; s += 64) {
+    const float* rec = base + s * stride;
+    if (rec[1] > 0.f) mx = fmaxf(mx, rec[0]);
   }
-  float num = 0.f, den = 0.f;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float den = 0.f;
+  for (int s = lane; s < sh.S; s += 64) {
+    const float* rec = base + s * stride;
+    if (rec[1] > 0.f) den = fmaf(exp2f(rec[0] - mx), rec[1], den);
+  }
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) den += __shfl_xor(den, off);
+  float num = 0.f;
+#pragma unroll 4
   for (int s = 0; s < sh.S; ++s) {
-    const float* rec = base + ((size_t)s * sh.G + g) * kRec;
-    if (!(rec[1] > 0.f)) continue;
-    float w = __expf(rec[0] - Mx);
-    den = fmaf(w, rec[1], den);
+    const float* rec = base + s * stride;
+    const float w = rec[1] > 0.f ? exp2f(rec[0] - mx) : 0.f;
     num = fmaf(w, rec[2 + j], num);
   }
   out[(size_t)hq_all * kD + j] = __float2half_rn(num / den);
 }
 
+// Splits of about kSplitRows rows, more and shorter ones when that leaves
+// fewer than kMinBlocks blocks; each split a multiple of one step of rows and
+// non-empty.
 Shape make_shape(int B, int Hq, int Hkv, int N) {
-  const int units = B * Hkv;
-  int S = (N + kMaxSplit - 1) / kMaxSplit;
-  while ((long)units * S < 2048 && (N + S * 2 - 1) / (S * 2) >= 128) S *= 2;
+  const long units = (long)B * Hkv;
+  int S = std::max((N + kSplitRows - 1) / kSplitRows, (int)std::min<long>(N, (kMinBlocks + units - 1) / units));
+  S = std::max(S, 1);
   int per = (N + S - 1) / S;
-  per = (per + 15) / 16 * 16;
-  if (per > kMaxSplit) per = kMaxSplit;
+  per = std::max(kStep, (per + kStep - 1) / kStep * kStep);
   S = (N + per - 1) / per;
   return Shape{B, Hq, Hkv, Hq / Hkv, N, S, per};
+}
+
+template <int G>
+hipError_t launch_split(const Shape& sh, const void* q, const void* k, const void* v, float sm_log2, float* part,
+                  hipStream_t st) {
+  CQ_LAUNCH(f16_split<G>, dim3(sh.S, sh.B * sh.Hkv), dim3(kThreads), 0, st, sh, (const __half*)q,
+            (const __half*)k, (const __half*)v, sm_log2, part);
+  return hipSuccess;
 }
 
 }  // namespace
@@ -212,8 +257,20 @@ hipError_t decode_fp16(const void* q, const void* k, const void* v, int B, int H
   if (B == 0) return hipSuccess;
   Shape sh = make_shape(B, Hq, Hkv, N);
   float* part = (float*)ws;
-  CQ_LAUNCH(f16_split, dim3(sh.S, B * Hkv), dim3(kThreads), 0, st, sh, (const __half*)q,
-                     (const __half*)k, (const __half*)v, sm_scale, part);
+  const float sl = sm_scale * 1.4426950408889634f;   // scores in the log2 domain
+  hipError_t e;
+  switch (sh.G) {
+    case 1: e = launch_split<1>(sh, q, k, v, sl, part, st); break;
+    case 2: e = launch_split<2>(sh, q, k, v, sl, part, st); break;
+    case 3: e = launch_split<3>(sh, q, k, v, sl, part, st); break;
+    case 4: e = launch_split<4>(sh, q, k, v, sl, part, st); break;
+    case 5: e = launch_split<5>(sh, q, k, v, sl, part, st); break;
+    case 6: e = launch_split<6>(sh, q, k, v, sl, part, st); break;
+    case 7: e = launch_split<7>(sh, q, k, v, sl, part, st); break;
+    case 8: e = launch_split<8>(sh, q, k, v, sl, part, st); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (e != hipSuccess) return e;
   CQ_LAUNCH(f16_merge, dim3(B * Hq), dim3(kD), 0, st, sh, part, (__half*)out);
   return hipSuccess;
 }

@@ -45,7 +45,9 @@ def test_calibrate_in_place_and_disabled():
     assert np.allclose(s.cpu().numpy(), exp, rtol=2e-7, atol=1e-7)
 
 
-@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 4, 1, 1), (2, 8, 2, 777), (3, 32, 8, 3392), (1, 8, 8, 2048)])
+@pytest.mark.parametrize("B,Hq,Hkv,N", [(1, 4, 1, 1), (2, 8, 2, 777), (3, 32, 8, 3392), (1, 8, 8, 2048),
+                                         (2, 6, 2, 65), (1, 16, 2, 130), (1, 7, 1, 63), (1, 10, 2, 5000),
+                                         (2, 24, 8, 8256)])
 def test_fp16_baseline_matches_textbook_attention(B, Hq, Hkv, N):
     import torch
     K = kv_numpy(40 + N, 0, ROLE_K, B, Hkv, N, 128)
