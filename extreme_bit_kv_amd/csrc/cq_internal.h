@@ -71,6 +71,13 @@ size_t decode_fast_ws(int B, int Hq, int Hkv, int n, int T, int d);
 bool decode_fast_supported(const DecodeArgs& a);
 hipError_t decode_fast(const DecodeArgs& a);
 
+// b = 1 as two launches over token chunks; `requested` chunks per unit, 0 = automatic
+bool decode_split_supported(const DecodeArgs& a);
+bool decode_split_preferred(const DecodeArgs& a, bool one_ok);   // the automatic choice
+size_t decode_split_ws(int B, int Hkv, int n, int T, int requested);
+size_t decode_split_ws_max(int B, int Hkv, int n, int T);
+hipError_t decode_split(const DecodeArgs& a, int requested);
+
 // ---- calibration --------------------------------------------------------
 hipError_t calibrate_rows(const float* scores, int R, int n, int enabled, float a_lo, float c_lo,
                           float a_hi, float c_hi, float* out, float* row_minmax, hipStream_t st);

@@ -37,6 +37,7 @@
 // The text tail (float K/V) is handled in plain float32 arithmetic.
 #include "cq_device.h"
 #include "cq_internal.h"
+#include "cq_mfma.h"
 
 namespace {
 
@@ -47,7 +48,23 @@ constexpr int kMaxTail = 256;
 constexpr int kPreTail = 64;          // tail tokens whose loads are issued early
 constexpr float kLog2e = 1.4426950408889634f;
 
-typedef int v4i __attribute__((ext_vector_type(4)));
+using cqm::v4i;
+using cqm::ld_any;
+using cqm::spread_lo;
+using cqm::spread_hi;
+using cqm::mfma;
+using cqm::gather_byte;
+using cqm::wave_sync_lds;
+using cqm::lds_barrier;
+
+// Every load of the kernels below is issued without a branch: at the join
+// of a branch around a load the compiler waits for it (and for everything
+// issued before it), which would serialize the prefetches.  Indices are
+// clamped into the tensor instead, and what they fetch past its end is
+// discarded where it is used.  An empty tensor (n == 0 or T == 0, possibly a
+// NULL pointer) is read at this 512-byte block instead: its base pointer is
+// selected once, and the clamped offsets of an empty tensor stay below 512 B.
+__device__ __align__(16) uint32_t g_pad[128];
 
 struct Params {
   const void* q;
@@ -66,44 +83,6 @@ struct Params {
   int calib_on;
   float a_lo, c_lo, a_hi, c_hi;
 };
-
-__device__ __forceinline__ float ld_any(const void* p, size_t i, int is_f32) {
-  return is_f32 ? reinterpret_cast<const float*>(p)[i] : __half2float(reinterpret_cast<const __half*>(p)[i]);
-}
-
-__device__ __forceinline__ v4i spread_lo(uint32_t w) {         // elements 0..15 of a packed word
-  v4i r;
-  r[0] = (int)(w & 0x01010101u);
-  r[1] = (int)((w >> 1) & 0x01010101u);
-  r[2] = (int)((w >> 2) & 0x01010101u);
-  r[3] = (int)((w >> 3) & 0x01010101u);
-  return r;
-}
-__device__ __forceinline__ v4i spread_hi(uint32_t w) {         // elements 16..31
-  v4i r;
-  r[0] = (int)((w >> 4) & 0x01010101u);
-  r[1] = (int)((w >> 5) & 0x01010101u);
-  r[2] = (int)((w >> 6) & 0x01010101u);
-  r[3] = (int)((w >> 7) & 0x01010101u);
-  return r;
-}
-
-__device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
-  return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
-}
-
-// byte `pl` of four registers, packed into one dword
-__device__ __forceinline__ uint32_t gather_byte(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3, int pl) {
-  const uint32_t lo = __builtin_amdgcn_perm(f1, f0, (uint32_t)pl | ((uint32_t)(pl + 4) << 8) | 0x0C0C0000u);
-  const uint32_t hi = __builtin_amdgcn_perm(f3, f2, 0x00000C0Cu | ((uint32_t)pl << 16) | ((uint32_t)(pl + 4) << 24));
-  return lo | hi;
-}
-
-__device__ __forceinline__ void wave_sync_lds() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // F32: query and text tail are float32 (else float16); the fast path takes
 // them in one dtype.
@@ -126,7 +105,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
-  __shared__ float s_tailred[kThreads / 128][4][128];   // tail values per token phase
+  __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
   __shared__ float s_vred[kWaves][4][128];      // per-wave value partials
   __shared__ float s_psum[kWaves][4];
 
@@ -134,18 +113,15 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int i16 = lane & 15, g4 = lane >> 4;    // A/B operand lane coordinates
   const int rh = i16 >> 2, rp = i16 & 3;        // A row = (head rh, plane rp)
   const int oh = lane >> 4;                     // output lane: head
-  const uint32_t* kc = P.kc;
-  auto load_k = [&](int t, uint4& w0, uint4& w1) {
-    const int tile = wave + kWaves * t;
-    const int tok = tile * kTile + 8 * i16;
-    if (tile < ntiles && tok < n) {
-      const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
-      w0 = src[0];
-      w1 = src[1];
-    } else {
-      w0 = make_uint4(0, 0, 0, 0);
-      w1 = make_uint4(0, 0, 0, 0);
-    }
+  const uint32_t* kc = n > 0 ? P.kc : g_pad;
+  const uint32_t* vcb = n > 0 ? P.vc : g_pad;
+  const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
+  const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
+  auto load_k = [&](int t, uint4& w0, uint4& w1) {   // tokens past n: scores not used
+    const int tok = max(min((wave + kWaves * t) * kTile + 8 * i16, n - 8), 0);
+    const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
+    w0 = src[0];
+    w1 = src[1];
   };
   uint4 kn0, kn1;                               // one key tile of look-ahead,
   load_k(0, kn0, kn1);                          // the first one under the prologue
@@ -175,7 +151,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       s_mqp[wave] = aq;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < 4) {
     const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
     const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
@@ -185,7 +161,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     s_inv2f[tid] = ldexpf(1.f, -F);
     s_c0[tid] = c0;
   }
-  __syncthreads();
+  lds_barrier();
   {
     const int hh = tid >> 7, j = tid & 127;
     const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
@@ -198,7 +174,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     ad[1 * 128 + j] = (unsigned char)d1;
     ad[2 * 128 + j] = (unsigned char)d2;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- phase 1: visual scores, their min and max -------------------------
   v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
@@ -254,81 +230,62 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   // score statistics settle ...  (The key base goes through an opaque copy:
   // otherwise the compiler proves the second pass's loads equal the first's and
   // keeps every first-pass score alive instead of recomputing it.)
-  asm("" : "+s"(kc));
-  load_k(0, kn0, kn1);
-  auto load_v = [&](int t, uint4& w0, uint4& w1) {
-    const int row = (wave + kWaves * t) * 4 + g4;   // V word row of this lane, channels 8*i16 .. +7
-    if (row < R) {
-      const uint4* src = reinterpret_cast<const uint4*>(P.vc + ((size_t)unit * R + row) * 128 + 8 * i16);
-      w0 = src[0];
-      w1 = src[1];
-    } else {
-      w0 = make_uint4(0, 0, 0, 0);
-      w1 = make_uint4(0, 0, 0, 0);
-    }
-  };
-  uint4 vn0, vn1;
-  load_v(0, vn0, vn1);
-  // ... and so are the first kPreTail tail tokens: keys as (token
-  // 4 wave + lane/16 + 32 r, channels 8 (lane%16) ..+7), values as (channel
-  // tid%128, tokens tid/128 + 4i).
+  // the first kPreTail tail keys, as (token 4 wave + lane/16 + 32 r, channels
+  // 8 (lane%16) ..+7), then the first key and value tiles of the second pass,
+  // then the first kPreTail tail values: requested in the order they are
+  // needed, since loads complete in order.
   const int tsub = lane >> 4, tcl = lane & 15;
   constexpr int kKtRounds = kPreTail / (4 * kWaves);
   uint4 ktp[kKtRounds][2];
 #pragma unroll
   for (int r = 0; r < kKtRounds; ++r) {
-    const int j = 4 * wave + tsub + 4 * kWaves * r;
-    ktp[r][0] = make_uint4(0, 0, 0, 0);
-    ktp[r][1] = make_uint4(0, 0, 0, 0);
-    if (j < T) {
-      if constexpr (F32) {
-        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(P.kt) +
-                                                          ((size_t)unit * T + j) * 128 + 8 * tcl);
-        ktp[r][0] = src[0];
-        ktp[r][1] = src[1];
-      } else {
-        ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
-                                                    ((size_t)unit * T + j) * 128 + 8 * tcl);
-      }
+    const int j = 4 * wave + tsub + 4 * kWaves * r;   // rows past T: scores not stored
+    const size_t e = ((size_t)unit * T + max(min(j, T - 1), 0)) * 128 + 8 * tcl;
+    if constexpr (F32) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+      ktp[r][0] = src[0];
+      ktp[r][1] = src[1];
+    } else {
+      ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(ktb) + e);
+      ktp[r][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  constexpr int kPhases = kThreads / 128;
-  const int vtj = tid & 127, vtq = tid >> 7;
-  float vtp[kPreTail / kPhases];
+  asm("" : "+s"(kc));
+  load_k(0, kn0, kn1);
+  // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
+  // tokens whose p is 0: whatever codes they read, their digits (-128, -128,
+  // 0) and the count row cancel in the product.
+  auto load_v = [&](int t, uint4& w0, uint4& w1) {
+    const int row = max(min((wave + kWaves * t) * 4 + g4, R - 1), 0);
+    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
+    w0 = src[0];
+    w1 = src[1];
+  };
+  uint4 vn0, vn1;
+  load_v(0, vn0, vn1);
+  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
+  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
+  constexpr int kPhases = kThreads / 64;
+  const int vcp = tid & 63, vph = tid >> 6;
+  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < kPreTail / kPhases; ++i) {
-    const int t = vtq + kPhases * i;
-    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32) : 0.f;
+    const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
+    if constexpr (F32) {
+      const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+      vtr[i][0] = x.x;
+      vtr[i][F32 ? 1 : 0] = x.y;
+    } else {
+      vtr[i][0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e);
+    }
   }
   // ---- text tail scores ---------------------------------------------------
+  // The prefetched rounds run straight (no early exit: every lane's rows were
+  // loaded, in bounds, and rows past T are not stored); rounds past kPreTail
+  // tokens load as they go.
   {
     const int sub = tsub, cl = tcl;
-#pragma unroll
-    for (int r = 0; r < kMaxTail / (4 * kWaves); ++r) {
-      const int j0 = 4 * wave + 4 * kWaves * r;
-      if (j0 >= T) break;
-      const int j = j0 + sub;
-      float kf[8];
-      if (r < kKtRounds) {                      // requested above
-        const uint4 ktp0 = ktp[r < kKtRounds ? r : 0][0], ktp1 = ktp[r < kKtRounds ? r : 0][1];
-        if constexpr (F32) {
-          kf[0] = __uint_as_float(ktp0.x); kf[1] = __uint_as_float(ktp0.y);
-          kf[2] = __uint_as_float(ktp0.z); kf[3] = __uint_as_float(ktp0.w);
-          kf[4] = __uint_as_float(ktp1.x); kf[5] = __uint_as_float(ktp1.y);
-          kf[6] = __uint_as_float(ktp1.z); kf[7] = __uint_as_float(ktp1.w);
-        } else {
-          const uint32_t hw[4] = {ktp0.x, ktp0.y, ktp0.z, ktp0.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
-            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
-      }
+    auto tail_scores = [&](int j, const float (&kf)[8]) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float s = 0.f;
@@ -340,6 +297,32 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
         s += __shfl_xor(s, 1);
         if (cl == 0 && j < T) s_ts[hh][j] = s;
       }
+    };
+#pragma unroll
+    for (int r = 0; r < kKtRounds; ++r) {
+      float kf[8];
+      if constexpr (F32) {
+        kf[0] = __uint_as_float(ktp[r][0].x); kf[1] = __uint_as_float(ktp[r][0].y);
+        kf[2] = __uint_as_float(ktp[r][0].z); kf[3] = __uint_as_float(ktp[r][0].w);
+        kf[4] = __uint_as_float(ktp[r][1].x); kf[5] = __uint_as_float(ktp[r][1].y);
+        kf[6] = __uint_as_float(ktp[r][1].z); kf[7] = __uint_as_float(ktp[r][1].w);
+      } else {
+        const uint32_t hw[4] = {ktp[r][0].x, ktp[r][0].y, ktp[r][0].z, ktp[r][0].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+          kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+        }
+      }
+      tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
+    }
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < T; j0 += 4 * kWaves) {
+      const int j = j0 + sub;
+      float kf[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
+      tail_scores(j, kf);
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
@@ -352,7 +335,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     s_red[wave][oh][0] = vmin;
     s_red[wave][oh][1] = vmax;
   }
-  __syncthreads();
+  lds_barrier();
   if (wave < G) {                               // wave hh settles head hh
     const int hh = wave;
     float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
@@ -388,26 +371,44 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
     if (lane == 0) s_ptail[hh] = pt;
   }
-  __syncthreads();
-  // text-tail values: thread (channel vtj, phase vtq) sums the tail tokens
-  // vtq + kPhases i for every head, the first kPreTail from the loads above
+  lds_barrier();
+  // text-tail values: thread (channel pair vcp, phase vph) sums the tail
+  // tokens vph + kPhases i for every head, the first kPreTail from the loads above
   {
-    float ta[4] = {0.f, 0.f, 0.f, 0.f};
+    float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
-      const int t = vtq + kPhases * i;
+      const int t = vph + kPhases * i;
       if (t < T) {
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = __uint_as_float(vtr[i][0]);
+          v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
+        } else {
+          v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
+          v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
+        }
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], vtp[i], ta[hh]);
+        for (int hh = 0; hh < G; ++hh) {
+          ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
+          ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+        }
       }
     }
-    for (int t = kPreTail + vtq; t < T; t += kPhases) {
-      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32);
+    for (int t = kPreTail + vph; t < T; t += kPhases) {
+      const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
+      const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], v, ta[hh]);
+      for (int hh = 0; hh < G; ++hh) {
+        ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
+        ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+      }
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) s_tailred[vtq][hh][vtj] = ta[hh];
+    for (int hh = 0; hh < G; ++hh) {
+      s_tailred[vph][hh][2 * vcp] = ta[hh][0];
+      s_tailred[vph][hh][2 * vcp + 1] = ta[hh][1];
+    }
   }
 
   // ---- phase 2: values ------------------------------------------------------
@@ -483,7 +484,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
-  __syncthreads();
+  lds_barrier();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     float sv = 0.f, pv = 0.f;
@@ -541,19 +542,22 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
-  __shared__ float s_tailred[kThreads / 128][4][128];
+  __shared__ float s_tailred[kThreads / 64][4][128];
   __shared__ float s_vred[kWaves][4][128];
   __shared__ float s_psum[kWaves][4];
 
   const int i16 = lane & 15, g4 = lane >> 4;
   const int rh = i16 >> 2, rp = i16 & 3;
   const int oh = lane >> 4;
-  const uint32_t* kc = P.kc;
-  auto load_k = [&](int tile, uint32_t (&w)[8]) {
-    const int tok0 = tile * TB + TPL * i16;
+  const uint32_t* kc = n > 0 ? P.kc : g_pad;
+  const uint32_t* vcb = n > 0 ? P.vc : g_pad;
+  const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
+  const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
+  auto load_k = [&](int tile, uint32_t (&w)[8]) {   // tokens past n: scores not used
+    const int tok0 = max(min(tile * TB + TPL * i16, n - TPL), 0);
 #pragma unroll
     for (int q = 0; q < 8; ++q) w[q] = 0u;
-    if (tile < tiles && tok0 < n) {
+    {
 #pragma unroll
       for (int p = 0; p < BITS; ++p) {
         const uint32_t* src = kc + ((size_t)unit * W + BITS * g4 + p) * n + tok0;
@@ -597,7 +601,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       s_mqp[wave] = aq;
     }
   }
-  __syncthreads();
+  lds_barrier();
   if (tid < 4) {
     const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
     const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
@@ -607,7 +611,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     s_inv2f[tid] = ldexpf(1.f, -F);
     s_c0[tid] = c0;
   }
-  __syncthreads();
+  lds_barrier();
   {
     const int hh = tid >> 7, j = tid & 127;
     const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
@@ -620,7 +624,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     ad[1 * 128 + j] = (unsigned char)d1;
     ad[2 * 128 + j] = (unsigned char)d2;
   }
-  __syncthreads();
+  lds_barrier();
 
   // ---- pass 1: visual scores, their min and max --------------------------
   v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
@@ -684,82 +688,58 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   // second pass: first key and value tiles requested now (the key base goes
   // through an opaque copy so that the compiler re-reads instead of keeping
   // first-pass values alive)
-  asm("" : "+s"(kc));
-  load_k(wave, kn);
-  auto load_v = [&](int tile, uint32_t (&w)[8]) {
-    const int row = tile * 4 + g4;
-    if (tile < tiles && row < R) {
-      const uint4* src = reinterpret_cast<const uint4*>(P.vc + ((size_t)unit * R + row) * 128 + 8 * i16);
-      const uint4 x0 = src[0], x1 = src[1];
-      w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
-      w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
-    } else {
-#pragma unroll
-      for (int q = 0; q < 8; ++q) w[q] = 0u;
-    }
-  };
-  uint32_t vn[8];
-  load_v(wave, vn);
-  // ... and so are the first kPreTail tail tokens: keys as (token
-  // 4 wave + lane/16 + 32 r, channels 8 (lane%16) ..+7), values as (channel
-  // tid%128, tokens tid/128 + 4i).
+  // tail keys, then the first key and value tiles of the second pass, then
+  // tail values, in the order they are needed (loads complete in order)
   const int tsub = lane >> 4, tcl = lane & 15;
   constexpr int kKtRounds = kPreTail / (4 * kWaves);
   uint4 ktp[kKtRounds][2];
 #pragma unroll
   for (int r = 0; r < kKtRounds; ++r) {
-    const int j = 4 * wave + tsub + 4 * kWaves * r;
-    ktp[r][0] = make_uint4(0, 0, 0, 0);
-    ktp[r][1] = make_uint4(0, 0, 0, 0);
-    if (j < T) {
-      if constexpr (F32) {
-        const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(P.kt) +
-                                                          ((size_t)unit * T + j) * 128 + 8 * tcl);
-        ktp[r][0] = src[0];
-        ktp[r][1] = src[1];
-      } else {
-        ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(P.kt) +
-                                                    ((size_t)unit * T + j) * 128 + 8 * tcl);
-      }
+    const int j = 4 * wave + tsub + 4 * kWaves * r;   // rows past T: scores not stored
+    const size_t e = ((size_t)unit * T + max(min(j, T - 1), 0)) * 128 + 8 * tcl;
+    if constexpr (F32) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+      ktp[r][0] = src[0];
+      ktp[r][1] = src[1];
+    } else {
+      ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(ktb) + e);
+      ktp[r][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  constexpr int kPhases = kThreads / 128;
-  const int vtj = tid & 127, vtq = tid >> 7;
-  float vtp[kPreTail / kPhases];
+  asm("" : "+s"(kc));
+  load_k(wave, kn);
+  auto load_v = [&](int tile, uint32_t (&w)[8]) {   // rows past the last: p = 0 (as in df_b1)
+    const int row = max(min(tile * 4 + g4, R - 1), 0);
+    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
+    const uint4 x0 = src[0], x1 = src[1];
+    w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
+    w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
+  };
+  uint32_t vn[8];
+  load_v(wave, vn);
+  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
+  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
+  constexpr int kPhases = kThreads / 64;
+  const int vcp = tid & 63, vph = tid >> 6;
+  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
 #pragma unroll
   for (int i = 0; i < kPreTail / kPhases; ++i) {
-    const int t = vtq + kPhases * i;
-    vtp[i] = t < T ? ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32) : 0.f;
+    const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
+    if constexpr (F32) {
+      const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+      vtr[i][0] = x.x;
+      vtr[i][F32 ? 1 : 0] = x.y;
+    } else {
+      vtr[i][0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e);
+    }
   }
   // ---- text tail scores ---------------------------------------------------
+  // The prefetched rounds run straight (no early exit: every lane's rows were
+  // loaded, in bounds, and rows past T are not stored); rounds past kPreTail
+  // tokens load as they go.
   {
     const int sub = tsub, cl = tcl;
-#pragma unroll
-    for (int r = 0; r < kMaxTail / (4 * kWaves); ++r) {
-      const int j0 = 4 * wave + 4 * kWaves * r;
-      if (j0 >= T) break;
-      const int j = j0 + sub;
-      float kf[8];
-      if (r < kKtRounds) {                      // requested above
-        const uint4 ktp0 = ktp[r < kKtRounds ? r : 0][0], ktp1 = ktp[r < kKtRounds ? r : 0][1];
-        if constexpr (F32) {
-          kf[0] = __uint_as_float(ktp0.x); kf[1] = __uint_as_float(ktp0.y);
-          kf[2] = __uint_as_float(ktp0.z); kf[3] = __uint_as_float(ktp0.w);
-          kf[4] = __uint_as_float(ktp1.x); kf[5] = __uint_as_float(ktp1.y);
-          kf[6] = __uint_as_float(ktp1.z); kf[7] = __uint_as_float(ktp1.w);
-        } else {
-          const uint32_t hw[4] = {ktp0.x, ktp0.y, ktp0.z, ktp0.w};
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
-            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
-          }
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < 8; ++c)
-          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
-      }
+    auto tail_scores = [&](int j, const float (&kf)[8]) {
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
         float s = 0.f;
@@ -771,6 +751,32 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
         s += __shfl_xor(s, 1);
         if (cl == 0 && j < T) s_ts[hh][j] = s;
       }
+    };
+#pragma unroll
+    for (int r = 0; r < kKtRounds; ++r) {
+      float kf[8];
+      if constexpr (F32) {
+        kf[0] = __uint_as_float(ktp[r][0].x); kf[1] = __uint_as_float(ktp[r][0].y);
+        kf[2] = __uint_as_float(ktp[r][0].z); kf[3] = __uint_as_float(ktp[r][0].w);
+        kf[4] = __uint_as_float(ktp[r][1].x); kf[5] = __uint_as_float(ktp[r][1].y);
+        kf[6] = __uint_as_float(ktp[r][1].z); kf[7] = __uint_as_float(ktp[r][1].w);
+      } else {
+        const uint32_t hw[4] = {ktp[r][0].x, ktp[r][0].y, ktp[r][0].z, ktp[r][0].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+          kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+        }
+      }
+      tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
+    }
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < T; j0 += 4 * kWaves) {
+      const int j = j0 + sub;
+      float kf[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
+      tail_scores(j, kf);
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
@@ -783,7 +789,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     s_red[wave][oh][0] = vmin;
     s_red[wave][oh][1] = vmax;
   }
-  __syncthreads();
+  lds_barrier();
   if (wave < G) {                               // wave hh settles head hh
     const int hh = wave;
     float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
@@ -819,26 +825,44 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
     if (lane == 0) s_ptail[hh] = pt;
   }
-  __syncthreads();
-  // text-tail values: thread (channel vtj, phase vtq) sums the tail tokens
-  // vtq + kPhases i for every head, the first kPreTail from the loads above
+  lds_barrier();
+  // text-tail values: thread (channel pair vcp, phase vph) sums the tail
+  // tokens vph + kPhases i for every head, the first kPreTail from the loads above
   {
-    float ta[4] = {0.f, 0.f, 0.f, 0.f};
+    float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
-      const int t = vtq + kPhases * i;
+      const int t = vph + kPhases * i;
       if (t < T) {
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = __uint_as_float(vtr[i][0]);
+          v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
+        } else {
+          v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
+          v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
+        }
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], vtp[i], ta[hh]);
+        for (int hh = 0; hh < G; ++hh) {
+          ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
+          ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+        }
       }
     }
-    for (int t = kPreTail + vtq; t < T; t += kPhases) {
-      const float v = ld_any(P.vt, ((size_t)unit * T + t) * 128 + vtj, F32);
+    for (int t = kPreTail + vph; t < T; t += kPhases) {
+      const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
+      const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) ta[hh] = fmaf(s_ts[hh][t], v, ta[hh]);
+      for (int hh = 0; hh < G; ++hh) {
+        ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
+        ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+      }
     }
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) s_tailred[vtq][hh][vtj] = ta[hh];
+    for (int hh = 0; hh < G; ++hh) {
+      s_tailred[vph][hh][2 * vcp] = ta[hh][0];
+      s_tailred[vph][hh][2 * vcp + 1] = ta[hh][1];
+    }
   }
 
   // ---- pass 2: values ------------------------------------------------------
@@ -928,7 +952,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
-  __syncthreads();
+  lds_barrier();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     float sv = 0.f, pv = 0.f;

@@ -85,12 +85,24 @@ typedef struct {
   float a_hi, c_hi;
 } cq_calib;
 
-/* Execution path selection, for tests and tuning (NULL opts = automatic). */
-typedef enum { CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2 } cq_path;
+/* Execution path selection, for tests and tuning (NULL opts = automatic).
+ * CQ_PATH_FAST picks one of the matrix-core decode schedules itself (the
+ * split one below 64 (batch, kv head) units or past 8192 tokens at b = 1,
+ * else the one-launch one); the two FAST_ values force one (decode only; for
+ * quantization they mean CQ_PATH_FAST):
+ *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head);
+ *   CQ_PATH_FAST_SPLIT  b = 1 only: a key-pass launch and a value-pass launch,
+ *                       each over token chunks of every (batch, kv head). */
+typedef enum {
+  CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4
+} cq_path;
 typedef struct {
-  int32_t path;     /* cq_path; CQ_PATH_FAST on an unsupported shape -> CQ_ERR_UNSUPPORTED */
+  int32_t path;     /* cq_path; a FAST path on an unsupported shape -> CQ_ERR_UNSUPPORTED */
   int32_t splits;   /* generic decode: token splits per (batch, kv head); 0 = automatic;
-                       clamped to [1, min(64, ceil(n/32))] */
+                       clamped to [1, min(64, ceil(n/32))].  Under CQ_PATH_AUTO a
+                       value > 0 selects the generic decode.  CQ_PATH_FAST_SPLIT:
+                       chunks per (batch, kv head), 0 = automatic, rounded so that
+                       a chunk is 4, 8, 16 or 32 tiles of 128 tokens. */
 } cq_opts;
 
 /* ABI version of the loaded library (CQ_ABI_VERSION). */

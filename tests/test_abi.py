@@ -85,6 +85,12 @@ def _decode(**kw):
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
+    (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0))), 1),              # no such path
+    (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),      # one-launch schedule: group sizes 1, 2, 4
+    (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), bits=2), 2),     # split schedule: b = 1 only
+    (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=0, kc=None, vc=None), 2),   # ... and n > 0
+    (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=96, ws=None), 3),           # it needs a workspace
+    (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=96, wsb=64), 3),
     (dict(kc=ODD), 1), (dict(vc=ODD), 1), (dict(kt=ODD), 1), (dict(ws=ODD), 1), (dict(q=ctypes.c_void_p(0x10001)), 1),
 ])
 def test_decode_rejects(kw, status):

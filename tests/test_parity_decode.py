@@ -14,15 +14,18 @@ SM = 1.0 / np.sqrt(128.0)
 RELATIVE = (0.9, 0.0, 0.8, 0.0)
 ABSOLUTE = (0.0, -4.0, 0.0, 4.0)
 IDENTITY = (1.0, 0.0, 1.0, 0.0)
-PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST]
+PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST, cqb.CQ_PATH_FAST_ONE, cqb.CQ_PATH_FAST_SPLIT]
+FAST_PATHS = (cqb.CQ_PATH_FAST, cqb.CQ_PATH_FAST_ONE, cqb.CQ_PATH_FAST_SPLIT)
 
 
-def fast_ok(q, K, kt, bits):
-    """Shapes the matrix-core decode kernels take (else CQ_ERR_UNSUPPORTED)."""
+def fast_ok(q, K, kt, bits, path=cqb.CQ_PATH_FAST):
+    """Shapes the matrix-core decode schedules take (else CQ_ERR_UNSUPPORTED)."""
     n, G = K.shape[2], q.shape[1] // K.shape[1]
     T = 0 if kt is None else kt.shape[2]
-    return (G in (1, 2, 4) and n % 32 == 0 and (bits > 1 or -(-n // 128) <= 64) and T <= 256
-            and (T == 0 or kt.dtype == q.dtype))
+    common = G in (1, 2, 4) and n % 32 == 0 and T <= 256 and (T == 0 or kt.dtype == q.dtype)
+    one = common and (bits > 1 or -(-n // 128) <= 64)
+    split = common and bits == 1 and n > 0
+    return {cqb.CQ_PATH_FAST_ONE: one, cqb.CQ_PATH_FAST_SPLIT: split}.get(path, one or split)
 
 
 def _run(K, V, q, kt, vt, bits, calib, path=cqb.CQ_PATH_AUTO, splits=0, out_dtype=None):
@@ -30,7 +33,7 @@ def _run(K, V, q, kt, vt, bits, calib, path=cqb.CQ_PATH_AUTO, splits=0, out_dtyp
     n = K.shape[2]
     kc, ks, km = cqb.cq_quantize_kv(K, bits, cqb.CQ_LAYOUT_K)
     vc, vs, vm = cqb.cq_quantize_kv(V, bits, cqb.CQ_LAYOUT_V)
-    if path == cqb.CQ_PATH_FAST and not fast_ok(q, K, kt, bits):
+    if path in FAST_PATHS and not fast_ok(q, K, kt, bits, path):
         with pytest.raises(cqb.CQError) as ei:
             cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=bits, sm_scale=SM, calib=calib,
                                path=path)
@@ -111,10 +114,16 @@ def test_split_count_does_not_change_the_result(splits):
 def test_tail_only(path):
     import torch
     _, _, q, kt, vt = draw_inputs(2, 8, 2, 0, 16, seed=9)
-    if path == cqb.CQ_PATH_FAST:
-        pytest.skip("covered by AUTO (n = 0 takes the matrix-core kernel)")
+    if path in (cqb.CQ_PATH_FAST, cqb.CQ_PATH_FAST_ONE):
+        pytest.skip("covered by AUTO (n = 0 takes the one-launch matrix-core kernel)")
     z = torch.zeros((2, 2, 128), dtype=torch.float32, device="cuda")
     note(f"decode n=0 T=16 path={path}")
+    if path == cqb.CQ_PATH_FAST_SPLIT:
+        with pytest.raises(cqb.CQError) as ei:
+            cqb.cq_decode_attn(q, None, z, z, None, z, z, kt, vt, n=0, bits=1, sm_scale=SM, calib=RELATIVE,
+                               path=path)
+        assert ei.value.status == 2
+        return
     out = cqb.cq_decode_attn(q, None, z, z, None, z, z, kt, vt, n=0, bits=1, sm_scale=SM, calib=RELATIVE,
                              path=path)
     torch.cuda.synchronize()
@@ -175,6 +184,15 @@ def test_long_context_sampled(path):
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE, [(0, 0), (40, 2), (63, 7)]), 4)
 
 
+@pytest.mark.parametrize("path", [cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST])
+def test_past_one_launch_limit(path):
+    """b = 1 beyond 64 key tiles (n = 16384): the automatic choice takes the split schedule."""
+    K, V, q, kt, vt = draw_inputs(2, 8, 2, 16384, 64, seed=15, host=False)
+    note(f"decode n=16384 path={path}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, path)
+    _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE, [(0, 1), (1, 0)]), 4)
+
+
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_bit_width_sweep_sampled(bits):
     """Bit-width sweep shape (B=32, n=3328), calibration off, sampled units."""
@@ -184,15 +202,58 @@ def test_bit_width_sweep_sampled(bits):
     _compare(got, _oracle(K, V, q, kt, vt, bits, None, [(0, 1), (31, 6)]), 4)
 
 
-@pytest.mark.parametrize("n", [32, 96, 128, 1024, 1152, 2048, 2080, 4096, 4224, 8192])
+@pytest.mark.parametrize("n", [32, 96, 128, 1024, 1152, 2048, 2080, 4096, 4224, 8192, 12320])
 @pytest.mark.parametrize("G", [1, 2, 4])
-def test_fast_kernel_tile_counts(n, G):
-    """Every instantiation of the matrix-core kernel (1, 2, 4 and 8 tiles per wave) on both sides of
-    each boundary, ragged tiles included."""
+@pytest.mark.parametrize("path", [cqb.CQ_PATH_FAST_ONE, cqb.CQ_PATH_FAST_SPLIT])
+def test_fast_kernel_tile_counts(n, G, path):
+    """Every instantiation of the one-launch kernel (1, 2, 4 and 8 tiles per wave) and of the split
+    kernels (1, 2, 4 and 8 tiles per wave) on both sides of each boundary, ragged tiles included."""
     K, V, q, kt, vt = draw_inputs(1, 2 * G, 2, n, 64, seed=n + G)
-    note(f"decode fast n={n} G={G}")
-    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST)
+    note(f"decode fast n={n} G={G} path={path}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, path)
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), G)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 3, 5, 9, 64])
+def test_split_chunk_counts(splits):
+    """Split decode at requested chunk counts (each rounded to 4, 8, 16 or 32 tiles per chunk): every
+    count agrees with the oracle and with every other count up to float32 summation order."""
+    import torch
+    K, V, q, kt, vt = draw_inputs(2, 8, 2, 2080, 64, seed=77)
+    note(f"decode split chunks={splits}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_SPLIT, splits, out_dtype=torch.float32)
+    _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
+    base = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_ONE, out_dtype=torch.float32)
+    diff = float(np.max(np.abs(got - base)))
+    assert diff <= 1e-5 * max(1.0, float(np.max(np.abs(base)))), f"max |diff| {diff:.3e}"
+
+
+@pytest.mark.parametrize("n", [32, 160, 1152, 4224, 8192])
+@pytest.mark.parametrize("splits", [1, 2, 4])
+def test_split_tiles_per_wave(n, splits):
+    """Few chunks per unit, so that every tiles-per-wave instantiation (up to 8) runs on short,
+    ragged and long contexts, G = 4."""
+    K, V, q, kt, vt = draw_inputs(1, 8, 2, n, 64, seed=n + 7 * splits)
+    note(f"decode split n={n} chunks={splits}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_SPLIT, splits)
+    _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
+
+
+def test_split_workspace_reused_across_calls():
+    """The split decode keeps its per-chunk partials in the workspace: three calls in a row on one
+    workspace, the second smaller, each match the oracle."""
+    import torch
+    ws = torch.empty(cqb.lib.cq_decode_attn_workspace(4, 16, 4, 4096, 64, 128, 1), dtype=torch.uint8,
+                     device="cuda")
+    for (B, n, seed) in [(4, 4096, 81), (2, 1024, 82), (4, 4096, 83)]:
+        K, V, q, kt, vt = draw_inputs(B, 16, 4, n, 64, seed=seed)
+        kc, ks, km = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
+        vc, vs, vm = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
+        note(f"decode split reused workspace B={B} n={n}")
+        out = cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=1, sm_scale=SM, calib=RELATIVE,
+                                 workspace=ws, path=cqb.CQ_PATH_FAST_SPLIT)
+        torch.cuda.synchronize()
+        _compare(out.float().cpu().numpy(), _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
