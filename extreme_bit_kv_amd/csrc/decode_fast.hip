@@ -7,9 +7,10 @@
 // head are mapped by the affine g fixed by their min and max before softmax.
 //
 // One workgroup (8 waves) per (batch, kv head); its query heads (G <= 4)
-// share every code it reads.  A wave owns 128-token tiles.  Two workgroups
-// fit on a CU, so a whole decode step (every unit of the batch) is resident
-// at once and one unit's reductions overlap another's loads.
+// share every code it reads.  The 128-token tiles are dealt to the waves as
+// they free up (an LDS counter per pass), so a wave whose loads return late
+// does not hold the others at the next barrier.  Two workgroups fit on a CU,
+// so a whole decode step (every unit of the batch) is resident at once.
 //
 // K side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16] with
 // v_mfma_i32_16x16x64_i8, twice (128 channels).  Rows of A are
@@ -32,7 +33,10 @@
 // planes.  Row 4h + 3 is all ones and counts the set code bits, which
 // restores the -128 offsets.  A lane produces the digits of 8 consecutive
 // tokens of one head, so one LDS write / read pair per wave hands them to the
-// lanes that feed A, already in the byte order of the packed V words.
+// lanes that feed A, already in the byte order of the packed V words.  The
+// planes combine into the exact integer sum_i P_i c_i, and the normalizer is
+// sum_i P_i (the same weights), both summed exactly: the result does not
+// depend on which wave took which tile.
 //
 // The text tail (float K/V) is handled in plain float32 arithmetic.
 #include "cq_device.h"
@@ -86,7 +90,7 @@ struct Params {
 
 // F32: query and text tail are float32 (else float16); the fast path takes
 // them in one dtype.
-template <int G, int MAXT, bool F32>
+template <int G, bool F32>
 __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int unit = blockIdx.x;
   const int b = unit / P.Hkv, h = unit % P.Hkv;
@@ -106,8 +110,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
   __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
-  __shared__ float s_vred[kWaves][4][128];      // per-wave value partials
-  __shared__ float s_psum[kWaves][4];
+  __shared__ unsigned long long s_vsum[4][128];   // sum P c per head and channel (2^-22 units)
+  __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
+  __shared__ int s_next[2];                        // next key tile of each pass
 
   // operand coordinates of the 16 x 16 x 64 products
   const int i16 = lane & 15, g4 = lane >> 4;    // A/B operand lane coordinates
@@ -117,14 +122,40 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const uint32_t* vcb = n > 0 ? P.vc : g_pad;
   const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
   const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
-  auto load_k = [&](int t, uint4& w0, uint4& w1) {   // tokens past n: scores not used
-    const int tok = max(min((wave + kWaves * t) * kTile + 8 * i16, n - 8), 0);
+  auto load_k = [&](int tile, uint4& w0, uint4& w1) {   // tokens past n: scores not used
+    const int tok = max(min(tile * kTile + 8 * i16, n - 8), 0);
     const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
     w0 = src[0];
     w1 = src[1];
   };
+  // The first kPreTail tail keys, as (token 4 wave + lane/16 + 32 r, channels
+  // 8 (lane%16) ..+7), are requested first: their scores are formed right
+  // after the prologue, while the first key tiles are still in flight.
+  const int tsub = lane >> 4, tcl = lane & 15;
+  constexpr int kKtRounds = kPreTail / (4 * kWaves);
+  uint4 ktp[kKtRounds][2];
+#pragma unroll
+  for (int r = 0; r < kKtRounds; ++r) {
+    const int j = 4 * wave + tsub + 4 * kWaves * r;   // rows past T: scores not stored
+    const size_t e = ((size_t)unit * T + max(min(j, T - 1), 0)) * 128 + 8 * tcl;
+    if constexpr (F32) {
+      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+      ktp[r][0] = src[0];
+      ktp[r][1] = src[1];
+    } else {
+      ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(ktb) + e);
+      ktp[r][1] = make_uint4(0, 0, 0, 0);
+    }
+  }
   uint4 kn0, kn1;                               // one key tile of look-ahead,
-  load_k(0, kn0, kn1);                          // the first one under the prologue
+  load_k(wave, kn0, kn1);                       // the first one under the prologue
+  // Tiles are dealt dynamically: wave w starts with tile w and then takes the
+  // next untaken one, so that a wave whose loads come back late does not hold
+  // up the workgroup at the next barrier.  (Results do not depend on which
+  // wave took which tile: min / max, and exact integer sums below.)
+  if (tid == 0) s_next[0] = s_next[1] = kWaves;
+  if (tid < 4) s_psum[tid] = 0.0;
+  for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
   // ---- prologue: post-scaled query, fixed-point digits -------------------
   __shared__ double s_c0p[8];
@@ -176,109 +207,6 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   }
   lds_barrier();
 
-  // ---- phase 1: visual scores, their min and max -------------------------
-  v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
-  if (rp < 3 && rh < G) {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
-    ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-    ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-  }
-  const float inv2f = s_inv2f[oh < G ? oh : 0];
-  const float c0f = (float)s_c0[oh < G ? oh : 0];
-  // scores of this lane's 8 tokens (head oh) from one key tile; the same
-  // integer products and the same rounding in both passes
-  auto scores = [&](const uint4& w0, const uint4& w1, float (&st)[8]) {
-    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
-#pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      v4i acc = {0, 0, 0, 0};
-      acc = mfma(ak0, spread_lo(wd[m]), acc);
-      acc = mfma(ak1, spread_hi(wd[m]), acc);
-      const int dot = acc[0] + (acc[1] << 8) + (acc[2] << 16);
-      st[m] = fmaf((float)dot, inv2f, c0f);
-      // pin the finished score: otherwise the compiler may keep the four
-      // accumulator registers alive in its place
-      asm volatile("" : "+v"(st[m]));
-    }
-  };
-  float vmin = INFINITY, vmax = -INFINITY;
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    const int tile = wave + kWaves * t;
-    const uint4 kw0 = kn0, kw1 = kn1;
-    if (t + 1 < MAXT) load_k(t + 1, kn0, kn1);
-    // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
-    const bool ok = tile < ntiles && tile * kTile + 8 * i16 < n;
-    float st[8];
-    scores(kw0, kw1, st);
-    float tmin = st[0], tmax = st[0];
-#pragma unroll
-    for (int m = 1; m < 8; ++m) {
-      tmin = fminf(tmin, st[m]);
-      tmax = fmaxf(tmax, st[m]);
-    }
-    if (ok) {
-      vmin = fminf(vmin, tmin);
-      vmax = fmaxf(vmax, tmax);
-    }
-    // fold tile by tile: left free, the compiler sinks these updates past the
-    // loop and keeps every tile's scores alive
-    asm volatile("" : "+v"(vmin), "+v"(vmax));
-  }
-  // the first key and value tiles of the second pass are requested before the
-  // score statistics settle ...  (The key base goes through an opaque copy:
-  // otherwise the compiler proves the second pass's loads equal the first's and
-  // keeps every first-pass score alive instead of recomputing it.)
-  // the first kPreTail tail keys, as (token 4 wave + lane/16 + 32 r, channels
-  // 8 (lane%16) ..+7), then the first key and value tiles of the second pass,
-  // then the first kPreTail tail values: requested in the order they are
-  // needed, since loads complete in order.
-  const int tsub = lane >> 4, tcl = lane & 15;
-  constexpr int kKtRounds = kPreTail / (4 * kWaves);
-  uint4 ktp[kKtRounds][2];
-#pragma unroll
-  for (int r = 0; r < kKtRounds; ++r) {
-    const int j = 4 * wave + tsub + 4 * kWaves * r;   // rows past T: scores not stored
-    const size_t e = ((size_t)unit * T + max(min(j, T - 1), 0)) * 128 + 8 * tcl;
-    if constexpr (F32) {
-      const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
-      ktp[r][0] = src[0];
-      ktp[r][1] = src[1];
-    } else {
-      ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(ktb) + e);
-      ktp[r][1] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  asm("" : "+s"(kc));
-  load_k(0, kn0, kn1);
-  // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
-  // tokens whose p is 0: whatever codes they read, their digits (-128, -128,
-  // 0) and the count row cancel in the product.
-  auto load_v = [&](int t, uint4& w0, uint4& w1) {
-    const int row = max(min((wave + kWaves * t) * 4 + g4, R - 1), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
-    w0 = src[0];
-    w1 = src[1];
-  };
-  uint4 vn0, vn1;
-  load_v(0, vn0, vn1);
-  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
-  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
-  constexpr int kPhases = kThreads / 64;
-  const int vcp = tid & 63, vph = tid >> 6;
-  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
-#pragma unroll
-  for (int i = 0; i < kPreTail / kPhases; ++i) {
-    const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
-    if constexpr (F32) {
-      const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
-      vtr[i][0] = x.x;
-      vtr[i][F32 ? 1 : 0] = x.y;
-    } else {
-      vtr[i][0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e);
-    }
-  }
   // ---- text tail scores ---------------------------------------------------
   // The prefetched rounds run straight (no early exit: every lane's rows were
   // loaded, in bounds, and rows past T are not stored); rounds past kPreTail
@@ -323,6 +251,92 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       for (int c = 0; c < 8; ++c)
         kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
       tail_scores(j, kf);
+    }
+  }
+  // ---- phase 1: visual scores, their min and max -------------------------
+  v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
+  if (rp < 3 && rh < G) {
+    const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
+    const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
+    ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+    ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  }
+  const float inv2f = s_inv2f[oh < G ? oh : 0];
+  const float c0f = (float)s_c0[oh < G ? oh : 0];
+  // scores of this lane's 8 tokens (head oh) from one key tile; the same
+  // integer products and the same rounding in both passes
+  auto scores = [&](const uint4& w0, const uint4& w1, float (&st)[8]) {
+    const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      v4i acc = {0, 0, 0, 0};
+      acc = mfma(ak0, spread_lo(wd[m]), acc);
+      acc = mfma(ak1, spread_hi(wd[m]), acc);
+      const int dot = acc[0] + (acc[1] << 8) + (acc[2] << 16);
+      st[m] = fmaf((float)dot, inv2f, c0f);
+      // pin the finished score: otherwise the compiler may keep the four
+      // accumulator registers alive in its place
+      asm volatile("" : "+v"(st[m]));
+    }
+  };
+  float vmin = INFINITY, vmax = -INFINITY;
+  for (int tile = wave; tile < ntiles;) {
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&s_next[0], 1);
+    nxt = __builtin_amdgcn_readfirstlane(nxt);
+    const uint4 kw0 = kn0, kw1 = kn1;
+    load_k(nxt, kn0, kn1);                      // past the last tile: an in-bounds reread, unused
+    // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
+    const bool ok = tile * kTile + 8 * i16 < n;
+    float st[8];
+    scores(kw0, kw1, st);
+    float tmin = st[0], tmax = st[0];
+#pragma unroll
+    for (int m = 1; m < 8; ++m) {
+      tmin = fminf(tmin, st[m]);
+      tmax = fmaxf(tmax, st[m]);
+    }
+    if (ok) {
+      vmin = fminf(vmin, tmin);
+      vmax = fmaxf(vmax, tmax);
+    }
+    // fold tile by tile: left free, the compiler sinks these updates past the
+    // loop and keeps every tile's scores alive
+    asm volatile("" : "+v"(vmin), "+v"(vmax));
+    tile = nxt;
+  }
+  // the first key and value tiles of the second pass, then the first
+  // kPreTail tail values, are requested before the score statistics settle.
+  // (The key base goes through an opaque copy: otherwise the compiler proves
+  // the second pass's loads equal the first's and keeps every first-pass score
+  // alive instead of recomputing it.)
+  asm("" : "+s"(kc));
+  load_k(wave, kn0, kn1);
+  // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
+  // tokens whose p is 0: whatever codes they read, their digits (-128, -128,
+  // 0) and the count row cancel in the product.
+  auto load_v = [&](int tile, uint4& w0, uint4& w1) {
+    const int row = max(min(tile * 4 + g4, R - 1), 0);
+    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
+    w0 = src[0];
+    w1 = src[1];
+  };
+  uint4 vn0, vn1;
+  load_v(wave, vn0, vn1);
+  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
+  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
+  constexpr int kPhases = kThreads / 64;
+  const int vcp = tid & 63, vph = tid >> 6;
+  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
+#pragma unroll
+  for (int i = 0; i < kPreTail / kPhases; ++i) {
+    const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
+    if constexpr (F32) {
+      const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+      vtr[i][0] = x.x;
+      vtr[i][F32 ? 1 : 0] = x.y;
+    } else {
+      vtr[i][0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e);
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
@@ -416,29 +430,30 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   v4i vacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
-  float psum = 0.f;
+  double psum = 0.0;                            // sum of this lane's P (exact: integers below 2^53)
   unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
-#pragma unroll
-  for (int t = 0; t < MAXT; ++t) {
-    const int tile = wave + kWaves * t;
-    if (tile >= ntiles) break;
+  for (int tile = wave; tile < ntiles;) {
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&s_next[1], 1);
+    nxt = __builtin_amdgcn_readfirstlane(nxt);
     const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
-    if (t + 1 < MAXT) {
-      load_k(t + 1, kn0, kn1);
-      load_v(t + 1, vn0, vn1);
-    }
+    load_k(nxt, kn0, kn1);
+    load_v(nxt, vn0, vn1);
     // probabilities of this lane's 8 tokens (head oh), as 22-bit fixed point
+    // P = round(p 2^22): the mantissa of p 2^22 + 2^23
     const bool ok = oh < G && tile * kTile + 8 * i16 < n;
     float st[8];
     scores(kw0, kw1, st);
-    uint32_t fb[8];
+    uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       float p = 0.f;
       if (ok) p = exp2f(fmaf(st[m], lam2, mu2));
-      psum += p;
-      fb[m] = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) ^ 0x00008080u;   // bytes: P^0x80, (P>>8)^0x80, P>>16
+      const uint32_t f = __float_as_uint(fmaf(p, 4194304.f, 8388608.f));
+      ptile += f & 0x007FFFFFu;
+      fb[m] = f ^ 0x00008080u;                   // bytes: P^0x80, (P>>8)^0x80, P>>16
     }
+    psum += (double)ptile;
     if (oh < G) {
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl) {
@@ -470,29 +485,30 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       vacc[ct] = mfma(av1, spread_hi(vwd[ct]), vacc[ct]);
     }
     wave_sync_lds();                       // digits read before the next tile overwrites them
+    tile = nxt;
   }
 
   // ---- combine planes, reduce over waves --------------------------------
-  // lane (head oh, column i16): channels 8*i16 + ct
+  // lane (head oh, column i16): channels 8*i16 + ct.  The planes combine into
+  // the exact integer sum_i P_i c_i, and the waves add theirs with 64-bit LDS
+  // atomics: exact, so the order in which waves arrive does not matter.
+  if (oh < G) {
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const float cnt128 = 128.f * (float)vacc[ct][3];
-    const float sv = ((float)vacc[ct][0] + cnt128) + 256.f * ((float)vacc[ct][1] + cnt128) +
-                     65536.f * (float)vacc[ct][2];
-    s_vred[wave][oh][8 * i16 + ct] = sv * (1.f / 4194304.f);
+    for (int ct = 0; ct < 8; ++ct) {
+      const long long cnt128 = 128ll * vacc[ct][3];
+      const long long sv = ((long long)vacc[ct][0] + cnt128) + 256ll * ((long long)vacc[ct][1] + cnt128) +
+                           65536ll * (long long)vacc[ct][2];
+      atomicAdd(&s_vsum[oh][8 * i16 + ct], (unsigned long long)sv);
+    }
   }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
-  if ((lane & 15) == 0) s_psum[wave][oh] = psum;
+  if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
   lds_barrier();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
-    float sv = 0.f, pv = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) {
-      sv += s_vred[w][hh][j];
-      pv += s_psum[w][hh];
-    }
+    const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 4194304.0));
+    const float pv = (float)(s_psum[hh] * (1.0 / 4194304.0));
     float tail = 0.f;
 #pragma unroll
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
@@ -976,21 +992,12 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
 
 
 
-template <int G, bool F32>
-hipError_t launch_g(const Params& p, int maxt, int units, hipStream_t st) {
-  switch (maxt) {
-    case 1: CQ_LAUNCH((df_b1<G, 1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-    case 2: CQ_LAUNCH((df_b1<G, 2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-    case 4: CQ_LAUNCH((df_b1<G, 4, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-    default: CQ_LAUNCH((df_b1<G, 8, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess;
-  }
-}
-
 template <bool F32>
-hipError_t launch_f(const Params& p, int G, int maxt, int units, hipStream_t st) {
-  if (G == 1) return launch_g<1, F32>(p, maxt, units, st);
-  if (G == 2) return launch_g<2, F32>(p, maxt, units, st);
-  return launch_g<4, F32>(p, maxt, units, st);
+hipError_t launch_f(const Params& p, int G, int units, hipStream_t st) {
+  if (G == 1) { CQ_LAUNCH((df_b1<1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_b1<2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_b1<4, F32>), dim3(units), dim3(kThreads), 0, st, p);
+  return hipSuccess;
 }
 
 template <int BITS, bool F32>
@@ -1016,10 +1023,9 @@ size_t decode_fast_ws(int, int, int, int, int, int) { return 0; }
 
 bool decode_fast_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
-  const int tiles = (a.n + kTile - 1) / kTile;
   return (a.bits == 1 || a.bits == 2 || a.bits == 4 || a.bits == 8) && a.d == 128 &&
-         (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && (a.bits > 1 || tiles <= 8 * kWaves) &&
-         a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
+         (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && a.T <= kMaxTail &&
+         (a.T == 0 || a.tail_dtype == a.q_dtype);
 }
 
 hipError_t decode_fast(const DecodeArgs& a) {
@@ -1028,14 +1034,12 @@ hipError_t decode_fast(const DecodeArgs& a) {
   Params p{a.q, a.k_codes, a.k_scale, a.k_min, a.v_codes, a.v_scale, a.v_min, a.k_tail, a.v_tail, a.out,
            a.Hq, a.Hkv, a.n, a.T, a.q_dtype == CQ_F32, a.tail_dtype == CQ_F32, a.out_dtype == CQ_F32,
            a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi};
-  const int tiles = (a.n + kTile - 1) / kTile;
-  const int maxt = tiles <= kWaves ? 1 : (tiles <= 2 * kWaves ? 2 : (tiles <= 4 * kWaves ? 4 : 8));
   const int G = a.Hq / a.Hkv;
   if (a.bits > 1)
     return a.q_dtype == CQ_F32 ? launch_b<true>(p, a.bits, G, units, a.stream)
                                : launch_b<false>(p, a.bits, G, units, a.stream);
-  return a.q_dtype == CQ_F32 ? launch_f<true>(p, G, maxt, units, a.stream)
-                             : launch_f<false>(p, G, maxt, units, a.stream);
+  return a.q_dtype == CQ_F32 ? launch_f<true>(p, G, units, a.stream)
+                             : launch_f<false>(p, G, units, a.stream);
 }
 
 }  // namespace cqi

@@ -377,9 +377,11 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   const int i16 = lane & 15, g4 = lane >> 4, rh = i16 >> 2, rp = i16 & 3, oh = lane >> 4;
   __shared__ QSmem qs;
   __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][32];   // [head][plane][128 token bytes]
-  __shared__ float s_vred[kWaves][4][128];
-  __shared__ float s_psum[kWaves][4];
+  __shared__ unsigned long long s_vsum[4][128];   // sum P c per head and channel (2^-22 units)
+  __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
   __shared__ float s_lam[4], s_mu[4], s_top[4];
+  if (tid < 4) s_psum[tid] = 0.0;
+  for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
   // requested in this order: query inputs, every chunk's min / max, then codes
   const QLoad ql = q_load<G, F32>(P, unit, b, h);
@@ -430,7 +432,7 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   v4i vacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
-  float psum = 0.f;
+  double psum = 0.0;                           // sum of this lane's P (exact: integers below 2^53)
   unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
 #pragma unroll
   for (int t = 0; t < MT; ++t) {
@@ -446,14 +448,17 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
     const bool okB = oh < G && tile * kTile + tok_of(i16, 4) < n;
     float st[8];
     tile_scores(ko, kw0, kw1, st);
-    uint32_t fb[8];
+    // P = round(p 2^22): the mantissa of p 2^22 + 2^23
+    uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       float p = 0.f;
       if (m < 4 ? okA : okB) p = exp2f(fmaf(st[m], lam2, mu2));
-      psum += p;
-      fb[m] = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) ^ 0x00008080u;   // bytes: P^0x80, (P>>8)^0x80, P>>16
+      const uint32_t f = __float_as_uint(fmaf(p, 4194304.f, 8388608.f));
+      ptile += f & 0x007FFFFFu;
+      fb[m] = f ^ 0x00008080u;                   // bytes: P^0x80, (P>>8)^0x80, P>>16
     }
+    psum += (double)ptile;
     if (oh < G) {
 #pragma unroll
       for (int pl = 0; pl < 3; ++pl) {
@@ -490,31 +495,27 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   }
 
   // ---- the chunk's record ------------------------------------------------
+  // exact integer sums, as in the one-launch kernel: the waves add theirs with
+  // 64-bit LDS atomics
+  if (oh < G) {
 #pragma unroll
-  for (int ct = 0; ct < 8; ++ct) {
-    const float cnt128 = 128.f * (float)vacc[ct][3];
-    const float sv = ((float)vacc[ct][0] + cnt128) + 256.f * ((float)vacc[ct][1] + cnt128) +
-                     65536.f * (float)vacc[ct][2];
-    s_vred[wave][oh][ch_of(i16, ct)] = sv * (1.f / 4194304.f);
+    for (int ct = 0; ct < 8; ++ct) {
+      const long long cnt128 = 128ll * vacc[ct][3];
+      const long long sv = ((long long)vacc[ct][0] + cnt128) + 256ll * ((long long)vacc[ct][1] + cnt128) +
+                           65536ll * (long long)vacc[ct][2];
+      atomicAdd(&s_vsum[oh][ch_of(i16, ct)], (unsigned long long)sv);
+    }
   }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
-  if (i16 == 0) s_psum[wave][oh] = psum;
+  if (i16 == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
   __syncthreads();
   float* rec = P.part + ((size_t)unit * (P.nc + 1) + chunk) * 4 * kPart;
   for (int idx = tid; idx < G * 128; idx += kThreads) {
     const int hh = idx >> 7, j = idx & 127;
-    float sv = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) sv += s_vred[w][hh][j];
-    rec[hh * kPart + j] = sv;
+    rec[hh * kPart + j] = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 4194304.0));
   }
-  if (tid < G) {
-    float pv = 0.f;
-#pragma unroll
-    for (int w = 0; w < kWaves; ++w) pv += s_psum[w][tid];
-    rec[tid * kPart + 128] = pv;
-  }
+  if (tid < G) rec[tid * kPart + 128] = (float)(s_psum[tid] * (1.0 / 4194304.0));
   if (chunk != 0) return;
 
   // ---- chunk 0: the text tail's record --------------------------------------
@@ -658,8 +659,8 @@ bool decode_split_supported(const DecodeArgs& a) {
 
 // The one-launch kernel runs one workgroup per (batch, kv head); with fewer
 // units than a quarter of the CUs most of the device would idle, and the
-// chunked launches are faster (measured: 8 units, n = 8192: 26 vs 32 us;
-// 64 units: 36 vs 33 us).  Beyond 64 key tiles only this schedule applies.
+// chunked launches are faster (measured at n = 8192: 8 units 26 vs 32 us,
+// 64 units 36 vs 33 us).
 bool decode_split_preferred(const DecodeArgs& a, bool one_ok) {
   return decode_split_supported(a) && (!one_ok || (long)a.B * a.Hkv < 64);
 }

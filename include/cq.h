@@ -87,9 +87,9 @@ typedef struct {
 
 /* Execution path selection, for tests and tuning (NULL opts = automatic).
  * CQ_PATH_FAST picks one of the matrix-core decode schedules itself (the
- * split one below 64 (batch, kv head) units or past 8192 tokens at b = 1,
- * else the one-launch one); the two FAST_ values force one (decode only; for
- * quantization they mean CQ_PATH_FAST):
+ * split one at b = 1 below 64 (batch, kv head) units, else the one-launch
+ * one); the two FAST_ values force one (decode only; for quantization they
+ * mean CQ_PATH_FAST):
  *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head);
  *   CQ_PATH_FAST_SPLIT  b = 1 only: a key-pass launch and a value-pass launch,
  *                       each over token chunks of every (batch, kv head). */

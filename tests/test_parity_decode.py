@@ -23,7 +23,7 @@ def fast_ok(q, K, kt, bits, path=cqb.CQ_PATH_FAST):
     n, G = K.shape[2], q.shape[1] // K.shape[1]
     T = 0 if kt is None else kt.shape[2]
     common = G in (1, 2, 4) and n % 32 == 0 and T <= 256 and (T == 0 or kt.dtype == q.dtype)
-    one = common and (bits > 1 or -(-n // 128) <= 64)
+    one = common
     split = common and bits == 1 and n > 0
     return {cqb.CQ_PATH_FAST_ONE: one, cqb.CQ_PATH_FAST_SPLIT: split}.get(path, one or split)
 
@@ -185,8 +185,8 @@ def test_long_context_sampled(path):
 
 
 @pytest.mark.parametrize("path", [cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST])
-def test_past_one_launch_limit(path):
-    """b = 1 beyond 64 key tiles (n = 16384): the automatic choice takes the split schedule."""
+def test_long_context_16k(path):
+    """b = 1 at n = 16384 (128 key tiles, 16 per wave of the one-launch kernel)."""
     K, V, q, kt, vt = draw_inputs(2, 8, 2, 16384, 64, seed=15, host=False)
     note(f"decode n=16384 path={path}")
     got = _run(K, V, q, kt, vt, 1, RELATIVE, path)
@@ -206,8 +206,9 @@ def test_bit_width_sweep_sampled(bits):
 @pytest.mark.parametrize("G", [1, 2, 4])
 @pytest.mark.parametrize("path", [cqb.CQ_PATH_FAST_ONE, cqb.CQ_PATH_FAST_SPLIT])
 def test_fast_kernel_tile_counts(n, G, path):
-    """Every instantiation of the one-launch kernel (1, 2, 4 and 8 tiles per wave) and of the split
-    kernels (1, 2, 4 and 8 tiles per wave) on both sides of each boundary, ragged tiles included."""
+    """The one-launch kernel (tiles dealt to its 8 waves as they free up) at fewer tiles than waves,
+    exactly one and several per wave, and the split kernels (1, 2, 4 and 8 tiles per wave) on both
+    sides of each boundary, ragged tiles included."""
     K, V, q, kt, vt = draw_inputs(1, 2 * G, 2, n, 64, seed=n + G)
     note(f"decode fast n={n} G={G} path={path}")
     got = _run(K, V, q, kt, vt, 1, RELATIVE, path)
