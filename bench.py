@@ -103,7 +103,7 @@ def source_digest(*names):
 
 KERNEL_SOURCES = {
     "quantize": ("quantize_fused.hip", "quantize_generic.hip", "cq_device.h"),
-    "decode": ("decode_fast.hip", "decode_generic.hip", "cq_device.h"),
+    "decode": ("decode_fast.hip", "decode_split.hip", "decode_generic.hip", "cq_device.h", "cq_mfma.h"),
 }
 
 
