@@ -259,6 +259,14 @@ def attend_dense(q, K, V, sm_scale):
     return _softmax_rows(s) @ np.asarray(V, np.float64)
 
 
+def visual_scores(q, k_codes, k_scale, k_min, sm_scale: float):
+    """Pre-softmax visual scores s_i = sm_scale * q . k_hat_i of G query heads
+    q[G, d] over one kv head's quantized keys, explicit-dequantization form
+    ([ART] Method part 2: k_hat_i = min_K + c_i * scale_K).  Returns [G, n]."""
+    q = np.asarray(q, np.float64)
+    return sm_scale * (q @ dequant(k_codes, k_scale, k_min).T)
+
+
 def decode_unit(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min,
                 k_tail, v_tail, sm_scale: float, calib: Optional[Calib]):
     """Decode attention of G query heads q[G, d] over one kv head.
@@ -280,9 +288,8 @@ def decode_unit(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min,
         raise ValueError("no tokens to attend over")
     parts_s, parts_v = [], []
     if n:
-        Kh = dequant(k_codes, k_scale, k_min)
         Vh = dequant(v_codes, v_scale, v_min)
-        s = sm_scale * (q @ Kh.T)
+        s = visual_scores(q, k_codes, k_scale, k_min, sm_scale)
         if calib is not None:
             s, _, _ = calibrate_rows(s, calib)
         parts_s.append(s)
