@@ -32,8 +32,8 @@ CQ_LAYOUT_K, CQ_LAYOUT_V = 0, 1
 CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT = 0, 1, 2, 3, 4
 
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
-            "cq_decode_attn_workspace", "cq_decode_attn", "cq_calibrate",
-            "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16")
+            "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
+            "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16")
 
 
 class cq_calib(ctypes.Structure):
@@ -64,6 +64,10 @@ lib.cq_decode_attn.restype = _i32
 lib.cq_decode_attn.argtypes = ([_vp, _i32] + [_vp] * 6 + [_vp, _vp, _i32] + [_i32] * 7 +
                                [_f32, ctypes.POINTER(cq_calib), _vp, _i32, _vp, _sz,
                                 ctypes.POINTER(cq_opts), _vp])
+lib.cq_visual_scores.restype = _i32
+lib.cq_visual_scores.argtypes = [_vp, _i32, _vp, _vp, _vp] + [_i32] * 6 + [_f32, _vp, _vp]
+lib.cq_scores_fp16.restype = _i32
+lib.cq_scores_fp16.argtypes = [_vp, _vp] + [_i32] * 5 + [_f32, _vp, _vp]
 lib.cq_calibrate.restype = _i32
 lib.cq_calibrate.argtypes = [_vp, _i32, _i32, ctypes.POINTER(cq_calib), _vp, _vp, _vp]
 lib.cq_decode_attn_fp16_workspace.restype = _sz
@@ -196,6 +200,41 @@ def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, 
                             _ptr(workspace), 0 if workspace is None else workspace.numel(),
                             ctypes.byref(opts), _stream(dev))
     _check(st, "cq_decode_attn")
+    return out
+
+
+def cq_visual_scores(q, k_codes, k_scale, k_min, *, n: int, bits: int, sm_scale: float, out=None):
+    """Pre-softmax visual scores (before g) from packed K codes: float32 [B, Hq, n]."""
+    torch = _torch()
+    _need(q, "q")
+    B, Hq, d = q.shape
+    Hkv = k_scale.shape[1]
+    _need(k_codes, "k_codes", code_words_shape(B, Hkv, n, d, bits, CQ_LAYOUT_K), torch.int32, q.device)
+    for name, t in (("k_scale", k_scale), ("k_min", k_min)):
+        _need(t, name, (B, Hkv, d), torch.float32, q.device)
+    if out is None:
+        out = torch.empty((B, Hq, n), dtype=torch.float32, device=q.device)
+    _need(out, "out", (B, Hq, n), torch.float32, q.device)
+    st = lib.cq_visual_scores(_ptr(q), _dtype_code(q), _ptr(k_codes), _ptr(k_scale), _ptr(k_min), B, Hq, Hkv, n,
+                              d, bits, float(sm_scale), _ptr(out), _stream(q.device))
+    _check(st, "cq_visual_scores")
+    return out
+
+
+def cq_scores_fp16(q, k, sm_scale: float, out=None):
+    """Exact scores over an unquantized cache: q [B, Hq, d], k [B, Hkv, N, d] float16 -> float32 [B, Hq, N]."""
+    torch = _torch()
+    _need(q, "q", None, torch.float16)
+    B, Hq, d = q.shape
+    _need(k, "k", None, torch.float16, q.device)
+    Hkv, N = k.shape[1], k.shape[2]
+    if tuple(k.shape) != (B, Hkv, N, d):
+        raise ValueError(f"k has shape {tuple(k.shape)}, expected {(B, Hkv, N, d)}")
+    if out is None:
+        out = torch.empty((B, Hq, N), dtype=torch.float32, device=q.device)
+    _need(out, "out", (B, Hq, N), torch.float32, q.device)
+    st = lib.cq_scores_fp16(_ptr(q), _ptr(k), B, Hq, Hkv, N, d, float(sm_scale), _ptr(out), _stream(q.device))
+    _check(st, "cq_scores_fp16")
     return out
 
 

@@ -172,6 +172,35 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
 }
 
 // ---------------------------------------------------------------------------
+cq_status cq_visual_scores(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
+                           const float* k_min, int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t d,
+                           int32_t bits, float sm_scale, float* scores, void* stream) {
+  if (!fits(B, Hq, n, d) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || d <= 0 || n < 1 || !valid_bits(bits) ||
+      !valid_dtype(q_dtype) || (d * bits) % 32 != 0 || !(sm_scale == sm_scale))
+    return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (q == nullptr || k_codes == nullptr || k_scale == nullptr || k_min == nullptr || scores == nullptr))
+    return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (!al16(k_codes) || !al4(q) || !al4(k_scale) || !al4(k_min) || !al4(scores)))
+    return CQ_ERR_INVALID_ARG;
+  if (d != cqi::kHeadDim || Hq / Hkv > 8) return CQ_ERR_UNSUPPORTED;
+  clear_stale_hip_error();
+  return from_hip(cqi::visual_scores(q, q_dtype, k_codes, k_scale, k_min, B, Hq, Hkv, n, bits, sm_scale, scores,
+                                     (hipStream_t)stream));
+}
+
+cq_status cq_scores_fp16(const void* q, const void* k, int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
+                         float sm_scale, float* scores, void* stream) {
+  if (!fits(B, Hkv, N, d) || !fits(B, Hq, N, 1) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || N < 1 || d <= 0 ||
+      !(sm_scale == sm_scale))
+    return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (q == nullptr || k == nullptr || scores == nullptr)) return CQ_ERR_INVALID_ARG;
+  if (B > 0 && (!al16(k) || !al4(q) || !al4(scores))) return CQ_ERR_INVALID_ARG;
+  if (d != cqi::kHeadDim || Hq / Hkv > 8) return CQ_ERR_UNSUPPORTED;
+  clear_stale_hip_error();
+  return from_hip(cqi::scores_fp16(q, k, B, Hq, Hkv, N, sm_scale, scores, (hipStream_t)stream));
+}
+
+// ---------------------------------------------------------------------------
 cq_status cq_calibrate(const float* scores, int32_t R, int32_t n, const cq_calib* calib, float* out,
                        float* row_minmax, void* stream) {
   if (R < 0 || n < 1 || (int64_t)R * n >= ((int64_t)1 << 40) || calib == nullptr) return CQ_ERR_INVALID_ARG;

@@ -78,6 +78,11 @@ size_t decode_split_ws(int B, int Hkv, int n, int T, int requested);
 size_t decode_split_ws_max(int B, int Hkv, int n, int T);
 hipError_t decode_split(const DecodeArgs& a, int requested);
 
+// visual scores only (generic kernel), float32 [B][Hq][n]
+hipError_t visual_scores(const void* q, int q_dtype, const uint32_t* k_codes, const float* k_scale,
+                         const float* k_min, int B, int Hq, int Hkv, int n, int bits, float sm_scale,
+                         float* scores, hipStream_t st);
+
 // ---- calibration --------------------------------------------------------
 hipError_t calibrate_rows(const float* scores, int R, int n, int enabled, float a_lo, float c_lo,
                           float a_hi, float c_hi, float* out, float* row_minmax, hipStream_t st);
@@ -86,5 +91,7 @@ hipError_t calibrate_rows(const float* scores, int R, int n, int enabled, float 
 size_t decode_fp16_ws(int B, int Hq, int Hkv, int N, int d);
 hipError_t decode_fp16(const void* q, const void* k, const void* v, int B, int Hq, int Hkv, int N,
                        int d, float sm_scale, void* out, void* ws, hipStream_t st);
+hipError_t scores_fp16(const void* q, const void* k, int B, int Hq, int Hkv, int N, float sm_scale, float* scores,
+                       hipStream_t st);
 
 }  // namespace cqi

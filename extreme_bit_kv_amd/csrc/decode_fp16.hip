@@ -222,6 +222,49 @@ __global__ void __launch_bounds__(kD) f16_merge(Shape sh, const float* __restric
   out[(size_t)hq_all * kD + j] = __float2half_rn(num / den);
 }
 
+// Scores only: scores[b][hq][i] = sm * q . k_i, float32, for the fp16 cache.
+// Block (64-token chunk, unit); a 16-lane group takes one row (16 B per
+// lane), as in the split kernel.
+template <int G>
+__global__ void __launch_bounds__(256) f16_scores(int Hq, int Hkv, int N, const __half* __restrict__ q,
+                                                  const __half* __restrict__ k, float sm,
+                                                  float* __restrict__ scores) {
+  const int unit = blockIdx.y;
+  const int b = unit / Hkv, h = unit % Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int sub = lane >> 4, cl = lane & 15;
+  uint4 qw[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {   // q is only 4-byte aligned
+    const uint32_t* qp = reinterpret_cast<const uint32_t*>(q + ((size_t)b * Hq + h * G + g) * kD + cl * 8);
+    qw[g] = make_uint4(qp[0], qp[1], qp[2], qp[3]);
+  }
+  const int t0 = blockIdx.x * 64 + wave * 16;
+  uint4 kr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+    kr[r] = *reinterpret_cast<const uint4*>(k + ((size_t)unit * N + min(t0 + r * 4 + sub, N - 1)) * kD + cl * 8);
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    float d[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float x = 0.f;
+      x = __builtin_amdgcn_fdot2(as_h2(qw[g].x), as_h2(kr[r].x), x, false);
+      x = __builtin_amdgcn_fdot2(as_h2(qw[g].y), as_h2(kr[r].y), x, false);
+      x = __builtin_amdgcn_fdot2(as_h2(qw[g].z), as_h2(kr[r].z), x, false);
+      x = __builtin_amdgcn_fdot2(as_h2(qw[g].w), as_h2(kr[r].w), x, false);
+      d[r] = x;
+    }
+    row_sum16(d);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int tok = t0 + r * 4 + sub;
+      if (cl == 0 && tok < N) scores[((size_t)b * Hq + h * G + g) * N + tok] = d[r] * sm;
+    }
+  }
+}
+
 // Splits of about kSplitRows rows, more and shorter ones when that leaves
 // fewer than kMinBlocks blocks; each split a multiple of one step of rows and
 // non-empty.
@@ -272,6 +315,26 @@ hipError_t decode_fp16(const void* q, const void* k, const void* v, int B, int H
   }
   if (e != hipSuccess) return e;
   CQ_LAUNCH(f16_merge, dim3(B * Hq), dim3(kD), 0, st, sh, part, (__half*)out);
+  return hipSuccess;
+}
+
+hipError_t scores_fp16(const void* q, const void* k, int B, int Hq, int Hkv, int N, float sm_scale, float* scores,
+                       hipStream_t st) {
+  if (B == 0 || N == 0) return hipSuccess;
+  const dim3 grid((N + 63) / 64, B * Hkv);
+  const __half* qh = (const __half*)q;
+  const __half* kh = (const __half*)k;
+  switch (Hq / Hkv) {
+    case 1: CQ_LAUNCH(f16_scores<1>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 2: CQ_LAUNCH(f16_scores<2>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 3: CQ_LAUNCH(f16_scores<3>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 4: CQ_LAUNCH(f16_scores<4>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 5: CQ_LAUNCH(f16_scores<5>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 6: CQ_LAUNCH(f16_scores<6>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 7: CQ_LAUNCH(f16_scores<7>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    case 8: CQ_LAUNCH(f16_scores<8>, grid, dim3(256), 0, st, Hq, Hkv, N, qh, kh, sm_scale, scores); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipSuccess;
 }
 

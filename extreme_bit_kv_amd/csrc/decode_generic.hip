@@ -90,6 +90,7 @@ __global__ void __launch_bounds__(kThreads) dg_scores(Shape sh, const QT* __rest
       }
     }
   }
+  if (mm == nullptr) return;                    // scores only (cq_visual_scores)
   __shared__ float rlo[kThreads], rhi[kThreads];
   for (int g = 0; g < G; ++g) {
     rlo[threadIdx.x] = lo[g];
@@ -332,6 +333,22 @@ size_t decode_generic_ws(int B, int Hq, int Hkv, int n, int T, int d, int S) {
 hipError_t decode_generic(const DecodeArgs& a) {
   const int S = decode_generic_splits(a.n, a.B * a.Hkv, a.splits);
   return a.q_dtype == CQ_F16 ? pick_tail<__half>(a, S) : pick_tail<float>(a, S);
+}
+
+hipError_t visual_scores(const void* q, int q_dtype, const uint32_t* k_codes, const float* k_scale,
+                         const float* k_min, int B, int Hq, int Hkv, int n, int bits, float sm_scale,
+                         float* scores, hipStream_t st) {
+  const int units = B * Hkv;
+  if (units == 0 || n == 0) return hipSuccess;
+  const int S = decode_generic_splits(n, units, 0);
+  Shape sh{B, Hq, Hkv, Hq / Hkv, n, 0, kD, bits, S};
+  if (q_dtype == CQ_F16)
+    CQ_LAUNCH(dg_scores<__half>, dim3(S, units), dim3(kThreads), 0, st, sh, (const __half*)q, k_codes, k_scale,
+              k_min, sm_scale, scores, (float2*)nullptr);
+  else
+    CQ_LAUNCH(dg_scores<float>, dim3(S, units), dim3(kThreads), 0, st, sh, (const float*)q, k_codes, k_scale,
+              k_min, sm_scale, scores, (float2*)nullptr);
+  return hipSuccess;
 }
 
 }  // namespace cqi

@@ -188,6 +188,21 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype,
                          const cq_opts* opts, void* stream);
 
 /* ------------------------------------------------------------------------
+ * cq_visual_scores — the pre-softmax visual scores of cq_decode_attn on their
+ * own, for inspection and diagnostics ([ART] Method part 2; before g):
+ *   scores[b][hq][i] = sm_scale*(q*k_scale).c_i + sm_scale*q.k_min,
+ * float32, from the packed K codes (any layout-K bit width).
+ *
+ *   q       device, [B][Hq][d] of q_dtype;  k_codes/k_scale/k_min as for decode
+ *   scores  device, float32 [B][Hq][n]
+ * Requires n >= 1, Hq % Hkv == 0, Hq/Hkv <= 8, d == 128 (else UNSUPPORTED).
+ * ------------------------------------------------------------------------ */
+cq_status cq_visual_scores(const void* q, cq_dtype q_dtype,
+                           const uint32_t* k_codes, const float* k_scale, const float* k_min,
+                           int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t d, int32_t bits,
+                           float sm_scale, float* scores, void* stream);
+
+/* ------------------------------------------------------------------------
  * cq_calibrate — the calibration map g on its own ([ART] Method part 3):
  * for every row r of scores[R][n], m = min, M = max, and
  * out[r][i] = g(scores[r][i]) as defined for cq_calib (computed in float64,
@@ -217,6 +232,13 @@ cq_status cq_decode_attn_fp16(const void* q, const void* k, const void* v,
                               int32_t B, int32_t Hq, int32_t Hkv, int32_t N, int32_t d,
                               float sm_scale, void* out,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* cq_scores_fp16 — the exact counterpart of cq_visual_scores, for the same
+ * diagnostics: scores[b][hq][i] = sm_scale * q.k_i (float32 accumulation) over an
+ * unquantized fp16 cache k [B][Hkv][N][d].  Requires N >= 1, Hq % Hkv == 0,
+ * Hq/Hkv <= 8, d == 128. */
+cq_status cq_scores_fp16(const void* q, const void* k, int32_t B, int32_t Hq, int32_t Hkv, int32_t N,
+                         int32_t d, float sm_scale, float* scores, void* stream);
 
 #ifdef __cplusplus
 }

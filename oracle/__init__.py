@@ -9,11 +9,11 @@ Parity pins live in ``tests/test_oracle_quant.py`` and
 parameters and target-interval definition, their tie rule and the precision of
 their stored scale (no page prints them).
 """
-from .cq_oracle import (Calib, attend_dense, calibrate_rows, code_bit_offset, decode_attn,
+from .cq_oracle import (Calib, attend_dense, calibrate_rows, dense_scores, code_bit_offset, decode_attn,
                         decode_unit, decode_unit_postscaled, dequant, exact_ints, nearest_f32,
                         pack, quantize, quantize_unit, unpack, visual_scores)
 from .brute import decode_brute, quantize_brute
 
-__all__ = ["Calib", "attend_dense", "calibrate_rows", "code_bit_offset", "decode_attn",
+__all__ = ["Calib", "attend_dense", "calibrate_rows", "dense_scores", "code_bit_offset", "decode_attn",
            "decode_unit", "decode_unit_postscaled", "dequant", "exact_ints", "nearest_f32",
            "pack", "quantize", "quantize_unit", "unpack", "visual_scores", "decode_brute", "quantize_brute"]

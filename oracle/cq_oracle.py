@@ -252,11 +252,14 @@ def _softmax_rows(z: np.ndarray) -> np.ndarray:
     return e / e.sum(axis=-1, keepdims=True)
 
 
+def dense_scores(q, K, sm_scale):
+    """Textbook pre-softmax scores sm_scale * q . k_i of q[G, d] over K[N, d] -> [G, N]."""
+    return sm_scale * (np.asarray(q, np.float64) @ np.asarray(K, np.float64).T)
+
+
 def attend_dense(q, K, V, sm_scale):
     """Textbook softmax attention for one kv head: q[G, d], K[N, d], V[N, d]."""
-    q = np.asarray(q, np.float64)
-    s = sm_scale * (q @ np.asarray(K, np.float64).T)
-    return _softmax_rows(s) @ np.asarray(V, np.float64)
+    return _softmax_rows(dense_scores(q, K, sm_scale)) @ np.asarray(V, np.float64)
 
 
 def visual_scores(q, k_codes, k_scale, k_min, sm_scale: float):

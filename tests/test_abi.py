@@ -126,3 +126,21 @@ def test_binding_has_no_cpu_fallback():
     assert "import oracle" not in src and "from oracle" not in src
     for f in os.listdir(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc")):
         assert "oracle" not in open(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc", f)).read()
+
+
+def test_score_entry_points_reject():
+    """cq_visual_scores / cq_scores_fp16 argument checks (no launch happens)."""
+    sm = 0.088
+    vs = lambda **kw: lib.cq_visual_scores(*[kw.get(k, v) for k, v in (
+        ("q", FAKE), ("qdt", 0), ("kc", FAKE), ("ks", FAKE), ("km", FAKE), ("B", 2), ("Hq", 32), ("Hkv", 8),
+        ("n", 64), ("d", 128), ("bits", 1), ("sm", sm), ("out", FAKE), ("st", None))])
+    assert vs(q=None) == 1 and vs(kc=None) == 1 and vs(out=None) == 1
+    assert vs(n=0) == 1 and vs(bits=3) == 1 and vs(Hq=30) == 1 and vs(qdt=2) == 1
+    assert vs(kc=ODD) == 1 and vs(sm=float("nan")) == 1
+    assert vs(d=64) == 2 and vs(Hq=80) == 2
+    f16 = lambda **kw: lib.cq_scores_fp16(*[kw.get(k, v) for k, v in (
+        ("q", FAKE), ("k", FAKE), ("B", 2), ("Hq", 32), ("Hkv", 8), ("N", 64), ("d", 128), ("sm", sm),
+        ("out", FAKE), ("st", None))])
+    assert f16(q=None) == 1 and f16(k=None) == 1 and f16(out=None) == 1 and f16(N=0) == 1
+    assert f16(k=ODD) == 1 and f16(Hq=30) == 1
+    assert f16(d=64) == 2 and f16(Hq=80) == 2
