@@ -36,6 +36,35 @@ __device__ __forceinline__ v4i spread_hi(uint32_t w) {
   return r;
 }
 
+// 1-bit words masked in place, one AND per register: element e (at bit
+// 8 (e mod 4) + floor(e / 4)) is left in byte e mod 4 of register
+// floor(e / 4) mod 4 as c_e 2^s(e), s(e) = min(floor(e / 4), 6).  The top bit
+// of each byte is moved down one place so that every byte is a non-negative
+// int8.  The other operand of the product carries 2^(7 - s(e)) for element e
+// (see bit_weight), so every product comes out as 2^7 c_e times its factor.
+__device__ __forceinline__ v4i bits_lo(uint32_t w) {
+  return v4i{(int)(w & 0x01010101u), (int)(w & 0x02020202u), (int)(w & 0x04040404u), (int)(w & 0x08080808u)};
+}
+__device__ __forceinline__ v4i bits_hi(uint32_t w) {
+  return v4i{(int)(w & 0x10101010u), (int)(w & 0x20202020u), (int)(w & 0x40404040u),
+             (int)((w >> 1) & 0x40404040u)};
+}
+// log2 of the compensating factor of element e of a word: 7 - s(e)
+__device__ __forceinline__ int bit_weight(int e) { return 7 - min((e >> 2) & 7, 6); }
+
+// 4 x 4 byte transpose: o_p holds byte p of f0, f1, f2, f3 (in that order)
+__device__ __forceinline__ void transpose_bytes(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3,
+                                                uint32_t& o0, uint32_t& o1, uint32_t& o2, uint32_t& o3) {
+  const uint32_t t0 = __builtin_amdgcn_perm(f1, f0, 0x05010400u);   // f0.0 f1.0 f0.1 f1.1
+  const uint32_t t1 = __builtin_amdgcn_perm(f1, f0, 0x07030602u);   // f0.2 f1.2 f0.3 f1.3
+  const uint32_t t2 = __builtin_amdgcn_perm(f3, f2, 0x05010400u);   // f2.0 f3.0 f2.1 f3.1
+  const uint32_t t3 = __builtin_amdgcn_perm(f3, f2, 0x07030602u);   // f2.2 f3.2 f2.3 f3.3
+  o0 = __builtin_amdgcn_perm(t2, t0, 0x05040100u);
+  o1 = __builtin_amdgcn_perm(t2, t0, 0x07060302u);
+  o2 = __builtin_amdgcn_perm(t3, t1, 0x05040100u);
+  o3 = __builtin_amdgcn_perm(t3, t1, 0x07060302u);
+}
+
 __device__ __forceinline__ v4i mfma(v4i a, v4i b, v4i c) {
   return __builtin_amdgcn_mfma_i32_16x16x64_i8(a, b, c, 0, 0, 0);
 }

@@ -56,6 +56,10 @@ using cqm::v4i;
 using cqm::ld_any;
 using cqm::spread_lo;
 using cqm::spread_hi;
+using cqm::bits_lo;
+using cqm::bits_hi;
+using cqm::bit_weight;
+using cqm::transpose_bytes;
 using cqm::mfma;
 using cqm::gather_byte;
 using cqm::wave_sync_lds;
@@ -104,8 +108,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ double s_c0[4];
   __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
-  __shared__ __align__(16) uint32_t s_adig[4][3][32];   // K-side A digits: [head][plane][128 channel bytes]
-  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][32];   // V-side A digits: [head][plane][128 token bytes]
+  __shared__ __align__(16) uint32_t s_adig[4][4][32];   // K-side A digits: [head][plane][128 channel bytes]
+  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // V-side A digits: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
@@ -147,13 +151,19 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       ktp[r][1] = make_uint4(0, 0, 0, 0);
     }
   }
-  uint4 kn0, kn1;                               // one key tile of look-ahead,
-  load_k(wave, kn0, kn1);                       // the first one under the prologue
+  // the key pass keeps two tiles of look-ahead per wave (kn, km), the value
+  // pass one (kn, vn); the first two are requested under the prologue
+  uint4 kn0, kn1, km0, km1;
+  load_k(wave, kn0, kn1);
+  load_k(wave + kWaves, km0, km1);
   // Tiles are dealt dynamically: wave w starts with tile w and then takes the
   // next untaken one, so that a wave whose loads come back late does not hold
   // up the workgroup at the next barrier.  (Results do not depend on which
   // wave took which tile: min / max, and exact integer sums below.)
-  if (tid == 0) s_next[0] = s_next[1] = kWaves;
+  if (tid == 0) {
+    s_next[0] = 2 * kWaves;
+    s_next[1] = kWaves;
+  }
   if (tid < 4) s_psum[tid] = 0.0;
   for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
@@ -189,21 +199,20 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     int F = 0;
     if (mq > 0.f) F = 21 - ilogbf(mq);
     s_F[tid] = F;
-    s_inv2f[tid] = ldexpf(1.f, -F);
+    s_inv2f[tid] = ldexpf(1.f, -F - 7);         // products carry 2^7 (bits_lo / bits_hi)
     s_c0[tid] = c0;
   }
   lds_barrier();
   {
+    // channel j's factor 2^bit_weight(j mod 32) makes up for the place its
+    // code bit keeps in the masked word; the digits are the bytes of
+    // Qs + 0x808080 with the low three offset back by 128 (signed base-256)
     const int hh = tid >> 7, j = tid & 127;
     const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
-    const int d0 = ((Q + 128) & 255) - 128;
-    const int Q1 = (Q - d0) >> 8;
-    const int d1 = ((Q1 + 128) & 255) - 128;
-    const int d2 = (Q1 - d1) >> 8;
+    const uint32_t dig = ((uint32_t)(Q * (1 << bit_weight(j & 31))) + 0x00808080u) ^ 0x00808080u;   // |Qs| <= 2^29
     unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
-    ad[0 * 128 + j] = (unsigned char)d0;
-    ad[1 * 128 + j] = (unsigned char)d1;
-    ad[2 * 128 + j] = (unsigned char)d2;
+#pragma unroll
+    for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + j] = (unsigned char)(dig >> (8 * pl));
   }
   lds_barrier();
 
@@ -255,7 +264,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   }
   // ---- phase 1: visual scores, their min and max -------------------------
   v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
-  if (rp < 3 && rh < G) {
+  if (rh < G) {
     const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
     const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
     ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
@@ -270,22 +279,28 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       v4i acc = {0, 0, 0, 0};
-      acc = mfma(ak0, spread_lo(wd[m]), acc);
-      acc = mfma(ak1, spread_hi(wd[m]), acc);
-      const int dot = acc[0] + (acc[1] << 8) + (acc[2] << 16);
-      st[m] = fmaf((float)dot, inv2f, c0f);
+      acc = mfma(ak0, bits_lo(wd[m]), acc);
+      acc = mfma(ak1, bits_hi(wd[m]), acc);
+      // 2^7 Q . c = lo + 2^16 hi; both halves fit 31 bits, the sum is
+      // rounded to float (the same operations in both passes)
+      const int lo = acc[0] + (acc[1] << 8), hi = acc[2] + (acc[3] << 8);
+      st[m] = fmaf(fmaf((float)hi, 65536.f, (float)lo), inv2f, c0f);
       // pin the finished score: otherwise the compiler may keep the four
       // accumulator registers alive in its place
       asm volatile("" : "+v"(st[m]));
     }
   };
   float vmin = INFINITY, vmax = -INFINITY;
-  for (int tile = wave; tile < ntiles;) {
+  // a wave's tiles come in increasing order: tile, then tnext (loading into
+  // km), then nxt
+  for (int tile = wave, tnext = wave + kWaves; tile < ntiles;) {
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&s_next[0], 1);
     nxt = __builtin_amdgcn_readfirstlane(nxt);
     const uint4 kw0 = kn0, kw1 = kn1;
-    load_k(nxt, kn0, kn1);                      // past the last tile: an in-bounds reread, unused
+    kn0 = km0;
+    kn1 = km1;
+    load_k(nxt, km0, km1);                      // past the last tile: an in-bounds reread, unused
     // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
     const bool ok = tile * kTile + 8 * i16 < n;
     float st[8];
@@ -303,7 +318,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     // fold tile by tile: left free, the compiler sinks these updates past the
     // loop and keeps every tile's scores alive
     asm volatile("" : "+v"(vmin), "+v"(vmax));
-    tile = nxt;
+    tile = tnext;
+    tnext = nxt;
   }
   // the first key and value tiles of the second pass, then the first
   // kPreTail tail values, are requested before the score statistics settle.
@@ -313,8 +329,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   asm("" : "+s"(kc));
   load_k(wave, kn0, kn1);
   // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
-  // tokens whose p is 0: whatever codes they read, their digits (-128, -128,
-  // 0) and the count row cancel in the product.
+  // tokens whose p is 0: whatever codes they read, their digits are 0.
   auto load_v = [&](int tile, uint4& w0, uint4& w1) {
     const int row = max(min(tile * 4 + g4, R - 1), 0);
     const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
@@ -427,9 +442,29 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 
   // ---- phase 2: values ------------------------------------------------------
   const float lam2 = s_lam[oh < G ? oh : 0], mu2 = s_mu[oh < G ? oh : 0];
+  // compensating factors of this lane's tokens 8 i16 + m (bits_lo / bits_hi):
+  // 2^wt0 for m < 4, 2^wt1 for m >= 4
+  const int wt0 = bit_weight(8 * i16), wt1 = bit_weight(8 * i16 + 4);
   v4i vacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
+  // the wave's int32 plane sums grow by at most 2^20 per tile (128 tokens x
+  // |digit| <= 128 x code byte <= 64); they are moved into the exact 64-bit
+  // LDS sums every kFlushTiles tiles, far below 2^31
+  constexpr int kFlushTiles = 256;
+  auto flush = [&]() {
+    if (oh < G) {
+#pragma unroll
+      for (int ct = 0; ct < 8; ++ct) {
+        const long long sv = (long long)vacc[ct][0] + 256ll * vacc[ct][1] + 65536ll * vacc[ct][2] +
+                             16777216ll * vacc[ct][3];
+        atomicAdd(&s_vsum[oh][8 * i16 + ct], (unsigned long long)sv);
+      }
+    }
+#pragma unroll
+    for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
+  };
+  int wtiles = 0;
   double psum = 0.0;                            // sum of this lane's P (exact: integers below 2^53)
   unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
   for (int tile = wave; tile < ntiles;) {
@@ -439,75 +474,65 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
     load_k(nxt, kn0, kn1);
     load_v(nxt, vn0, vn1);
-    // probabilities of this lane's 8 tokens (head oh), as 22-bit fixed point
-    // P = round(p 2^22): the mantissa of p 2^22 + 2^23
+    // probabilities of this lane's 8 tokens (head oh) as 22-bit fixed point
+    // P = round(p 2^22), the mantissa of p 2^22 + 2^23; tokens that do not
+    // count get exponent -inf, so p = 0
     const bool ok = oh < G && tile * kTile + 8 * i16 < n;
+    const float mu_t = ok ? mu2 : -INFINITY;
     float st[8];
     scores(kw0, kw1, st);
     uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      float p = 0.f;
-      if (ok) p = exp2f(fmaf(st[m], lam2, mu2));
-      const uint32_t f = __float_as_uint(fmaf(p, 4194304.f, 8388608.f));
-      ptile += f & 0x007FFFFFu;
-      fb[m] = f ^ 0x00008080u;                   // bytes: P^0x80, (P>>8)^0x80, P>>16
+      const float p = __builtin_amdgcn_exp2f(fmaf(st[m], lam2, mu_t));   // argument <= 0 (up to rounding)
+      const uint32_t Pm = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) & 0x007FFFFFu;
+      ptile += Pm;
+      // digits of P 2^wt: bytes of P 2^wt + 0x808080, the low three offset back by 128
+      fb[m] = ((Pm << (m < 4 ? wt0 : wt1)) + 0x00808080u) ^ 0x00808080u;
     }
     psum += (double)ptile;
     if (oh < G) {
+      uint32_t d[2][4];
+      transpose_bytes(fb[0], fb[1], fb[2], fb[3], d[0][0], d[0][1], d[0][2], d[0][3]);
+      transpose_bytes(fb[4], fb[5], fb[6], fb[7], d[1][0], d[1][1], d[1][2], d[1][3]);
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        const uint32_t d0 = gather_byte(fb[0], fb[1], fb[2], fb[3], pl);
-        const uint32_t d1 = gather_byte(fb[4], fb[5], fb[6], fb[7], pl);
-        *reinterpret_cast<uint2*>(pd + (oh * 3 + pl) * 128 + 8 * i16) = make_uint2(d0, d1);
-      }
+      for (int pl = 0; pl < 4; ++pl)
+        *reinterpret_cast<uint2*>(pd + (oh * 4 + pl) * 128 + 8 * i16) = make_uint2(d[0][pl], d[1][pl]);
     }
     wave_sync_lds();
-    v4i av0, av1;
-    if (rp < 3) {
-      if (rh < G) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(pd + (rh * 3 + rp) * 128 + 32 * g4);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(pd + (rh * 3 + rp) * 128 + 32 * g4 + 16);
-        av0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-        av1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      } else {
-        av0 = v4i{0, 0, 0, 0};
-        av1 = av0;
-      }
-    } else {
-      av0 = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-      av1 = av0;
+    v4i av0 = {0, 0, 0, 0}, av1 = {0, 0, 0, 0};
+    if (rh < G) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(pd + (rh * 4 + rp) * 128 + 32 * g4);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(pd + (rh * 4 + rp) * 128 + 32 * g4 + 16);
+      av0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+      av1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
     const uint32_t vwd[8] = {vw0.x, vw0.y, vw0.z, vw0.w, vw1.x, vw1.y, vw1.z, vw1.w};
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      vacc[ct] = mfma(av0, spread_lo(vwd[ct]), vacc[ct]);
-      vacc[ct] = mfma(av1, spread_hi(vwd[ct]), vacc[ct]);
+      vacc[ct] = mfma(av0, bits_lo(vwd[ct]), vacc[ct]);
+      vacc[ct] = mfma(av1, bits_hi(vwd[ct]), vacc[ct]);
     }
     wave_sync_lds();                       // digits read before the next tile overwrites them
+    if (++wtiles == kFlushTiles) {
+      flush();
+      wtiles = 0;
+    }
     tile = nxt;
   }
 
   // ---- combine planes, reduce over waves --------------------------------
   // lane (head oh, column i16): channels 8*i16 + ct.  The planes combine into
-  // the exact integer sum_i P_i c_i, and the waves add theirs with 64-bit LDS
-  // atomics: exact, so the order in which waves arrive does not matter.
-  if (oh < G) {
-#pragma unroll
-    for (int ct = 0; ct < 8; ++ct) {
-      const long long cnt128 = 128ll * vacc[ct][3];
-      const long long sv = ((long long)vacc[ct][0] + cnt128) + 256ll * ((long long)vacc[ct][1] + cnt128) +
-                           65536ll * (long long)vacc[ct][2];
-      atomicAdd(&s_vsum[oh][8 * i16 + ct], (unsigned long long)sv);
-    }
-  }
+  // the exact integer 2^7 sum_i P_i c_i, and the waves add theirs with 64-bit
+  // LDS atomics: exact, so the order in which waves arrive does not matter.
+  flush();
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
   lds_barrier();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
-    const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 4194304.0));
+    const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 536870912.0));   // 2^-29
     const float pv = (float)(s_psum[hh] * (1.0 / 4194304.0));
     float tail = 0.f;
 #pragma unroll

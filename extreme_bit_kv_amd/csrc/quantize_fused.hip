@@ -387,9 +387,14 @@ namespace cqi {
 
 size_t quant_fused_ws(int B, int H, int n, int d) { return ws_bytes(B * H, (n + kChunk - 1) / kChunk); }
 
+// All chunks of a unit must be resident together, so a unit may have at most
+// as many chunks as the device holds workgroups of the kernel at once.
 bool quant_fused_supported(const QuantArgs& a) {
-  return a.dtype == CQ_F16 && a.bits == 1 && a.d == 128 && a.n >= 1 && a.n <= (1 << 20) &&
-         (long)a.B * a.H >= 1;
+  if (!(a.dtype == CQ_F16 && a.bits == 1 && a.d == 128 && a.n >= 1 && a.n <= (1 << 20) &&
+        (long)a.B * a.H >= 1))
+    return false;
+  const void* fn = a.layout == CQ_LAYOUT_K ? (const void*)qf_b1<CQ_LAYOUT_K> : (const void*)qf_b1<CQ_LAYOUT_V>;
+  return capacity_of(fn, a.layout == CQ_LAYOUT_K ? 0 : 1) >= (a.n + kChunk - 1) / kChunk;
 }
 
 hipError_t quant_fused(const QuantArgs& a) {

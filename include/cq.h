@@ -136,6 +136,10 @@ const char* cq_status_str(cq_status s);
  *             than the device holds at once; a time-out needs other work to
  *             keep part of the device busy for seconds.  CQ_PATH_GENERIC has
  *             no such wait.
+ *   The fused path takes fp16 input at b = 1 when every 512-token chunk of a
+ *   (b, h) fits on the device at once (n <= 512 x the co-resident workgroups,
+ *   262144 tokens on a 256-CU MI355X); otherwise CQ_PATH_AUTO uses the
+ *   generic kernels and CQ_PATH_FAST returns CQ_ERR_UNSUPPORTED.
  *
  * For each (b, h, channel j) with mn = min_i x, mx = max_i x over the n tokens:
  *   code(i, j) = round-half-to-even((x_ij - mn)*L/(mx - mn)), decided exactly;

@@ -193,6 +193,16 @@ def test_long_context_16k(path):
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE, [(0, 1), (1, 0)]), 4)
 
 
+@pytest.mark.parametrize("path", [cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST_ONE])
+def test_long_context_270k(path):
+    """b = 1 at n = 270016 (2110 key tiles, about 264 per wave): each wave's
+    int32 plane sums are moved into the 64-bit sums at least once on the way."""
+    K, V, q, kt, vt = draw_inputs(1, 4, 1, 270016, 64, seed=16, host=False)
+    note(f"decode n=270016 path={path}")
+    got = _run(K, V, q, kt, vt, 1, RELATIVE, path)
+    _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
+
+
 @pytest.mark.parametrize("bits", [2, 4, 8])
 def test_bit_width_sweep_sampled(bits):
     """Bit-width sweep shape (B=32, n=3328), calibration off, sampled units."""

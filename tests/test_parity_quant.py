@@ -13,9 +13,14 @@ PATHS = [cqb.CQ_PATH_GENERIC, cqb.CQ_PATH_AUTO, cqb.CQ_PATH_FAST]
 LAYOUTS = {cqb.CQ_LAYOUT_K: "K", cqb.CQ_LAYOUT_V: "V"}
 
 
+# one (batch, head) of the fused kernel spans at most this many tokens on a
+# 256-CU MI355X: 512-token chunks, all resident at once, 2 workgroups per CU
+FUSED_MAX_N = 512 * 512
+
+
 def _fast_ok(x_dev, bits):
     import torch
-    return x_dev.dtype == torch.float16 and bits == 1 and x_dev.shape[2] >= 1
+    return x_dev.dtype == torch.float16 and bits == 1 and 1 <= x_dev.shape[2] <= FUSED_MAX_N
 
 
 def _check_units(x_dev, bits, layout, path, units=None):
@@ -114,6 +119,15 @@ def test_long_context_sampled_units(path):
     units = [(0, 0), (31, 4), (63, 7)]
     _check_units(K, 1, 0, path, units)
     _check_units(V, 1, 1, path, units)
+
+
+@pytest.mark.parametrize("layout", [0, 1])
+@pytest.mark.parametrize("path", PATHS)
+def test_longer_than_one_fused_round(layout, path):
+    """n = 270016 has more 512-token chunks per head (528) than the device
+    holds workgroups: AUTO takes the generic kernels, FAST is refused."""
+    x, _, _, _, _ = draw_inputs(1, 4, 1, 270016, 0, seed=17, host=False)
+    _check_units(x, 1, layout, path)
 
 
 def test_fused_repeated_launches_are_identical():
