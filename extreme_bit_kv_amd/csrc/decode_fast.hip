@@ -102,6 +102,11 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int n = P.n, T = P.T;
   const int ntiles = (n + kTile - 1) / kTile;
   const int R = n >> 5;
+  // Issue priority: the two workgroups on a CU would otherwise run their key
+  // passes unevenly (the older one first), leaving the other's value pass
+  // alone at the end.  High through the key pass (latency-bound), low through
+  // the value pass (compute-bound), medium for the final reduction.
+  __builtin_amdgcn_s_setprio(3);
 
   __shared__ float s_q[4][128];                 // sm * q, float
   __shared__ float s_qp[4][128];                // sm * q * scale_K
@@ -114,9 +119,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
   __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
-  __shared__ unsigned long long s_vsum[4][128];   // sum P c per head and channel (2^-22 units)
+  __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
   __shared__ int s_next[2];                        // next key tile of each pass
+  __shared__ float s_vs[128], s_vm[128];           // scale_V, min_V
 
   // operand coordinates of the 16 x 16 x 64 products
   const int i16 = lane & 15, g4 = lane >> 4;    // A/B operand lane coordinates
@@ -126,6 +132,18 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const uint32_t* vcb = n > 0 ? P.vc : g_pad;
   const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
   const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
+  // The prologue's inputs are requested before any prefetch: vector loads
+  // complete in order, so the prologue then waits for these alone.  Thread:
+  // head ph (heads past G read head G - 1, unused), channel pj; the scales and
+  // minima of an empty cache are read at the zero block.
+  const int ph = tid >> 7, pj = tid & 127;
+  const float* ksb = n > 0 ? P.ks : reinterpret_cast<const float*>(g_pad);
+  const float* kmb = n > 0 ? P.km : reinterpret_cast<const float*>(g_pad);
+  const float* vsb = n > 0 ? P.vs : reinterpret_cast<const float*>(g_pad);
+  const float* vmb = n > 0 ? P.vm : reinterpret_cast<const float*>(g_pad);
+  const size_t prm = n > 0 ? (size_t)unit * 128 + pj : (size_t)pj;
+  const float q_in = ld_any(P.q, ((size_t)b * P.Hq + h * G + min(ph, G - 1)) * 128 + pj, F32);
+  const float ks_in = ksb[prm], km_in = kmb[prm], vs_in = vsb[prm], vm_in = vmb[prm];
   auto load_k = [&](int tile, uint4& w0, uint4& w1) {   // tokens past n: scores not used
     const int tok = max(min(tile * kTile + 8 * i16, n - 8), 0);
     const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
@@ -170,17 +188,21 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   // ---- prologue: post-scaled query, fixed-point digits -------------------
   __shared__ double s_c0p[8];
   __shared__ float s_mqp[8];
-  {                                             // thread: head tid / 128, channel tid % 128
-    const int hh = tid >> 7, j = tid & 127;
+  {                                             // thread: head ph, channel pj
+    const int hh = ph, j = pj;
     float qv = 0.f, qp = 0.f;
     double pr = 0.0;
     if (hh < G) {
-      qv = P.sm * ld_any(P.q, ((size_t)b * P.Hq + h * G + hh) * 128 + j, F32);
-      qp = qv * P.ks[(size_t)unit * 128 + j];
-      pr = (double)qv * (double)P.km[(size_t)unit * 128 + j];
+      qv = P.sm * q_in;
+      qp = qv * ks_in;
+      pr = (double)qv * (double)km_in;
     }
     s_q[hh][j] = qv;
     s_qp[hh][j] = qp;
+    if (hh == 0) {
+      s_vs[j] = vs_in;
+      s_vm[j] = vm_in;
+    }
     float aq = fabsf(qp);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
@@ -441,6 +463,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   }
 
   // ---- phase 2: values ------------------------------------------------------
+  __builtin_amdgcn_s_setprio(0);
   const float lam2 = s_lam[oh < G ? oh : 0], mu2 = s_mu[oh < G ? oh : 0];
   // compensating factors of this lane's tokens 8 i16 + m (bits_lo / bits_hi):
   // 2^wt0 for m < 4, 2^wt1 for m >= 4
@@ -522,6 +545,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   }
 
   // ---- combine planes, reduce over waves --------------------------------
+  __builtin_amdgcn_s_setprio(1);
   // lane (head oh, column i16): channels 8*i16 + ct.  The planes combine into
   // the exact integer 2^7 sum_i P_i c_i, and the waves add theirs with 64-bit
   // LDS atomics: exact, so the order in which waves arrive does not matter.
@@ -539,7 +563,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
     const float pt = s_ptail[hh];
     float o = tail;
-    if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
+    if (n > 0) o += s_vs[j] * sv + pv * s_vm[j];
     o /= (pv + pt);
     const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
     if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
