@@ -37,6 +37,7 @@ import glob
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -94,10 +95,19 @@ def fp16_bytes(cfg):
     return units * (2 * (cfg.n + cfg.T) * cfg.d * 2 + 2 * G * cfg.d * 2)
 
 
+def _code_only(text):
+    """Source text without comments and blank space: a comment edit leaves
+    the kernel, and so the counters taken on it, unchanged."""
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
 def source_digest(*names):
     h = hashlib.sha256()
     for name in names:
-        h.update(open(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc", name), "rb").read())
+        with open(os.path.join(ROOT, "extreme_bit_kv_amd", "csrc", name)) as fh:
+            h.update(_code_only(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

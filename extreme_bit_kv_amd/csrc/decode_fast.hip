@@ -13,30 +13,32 @@
 // so a whole decode step (every unit of the batch) is resident at once.
 //
 // K side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16] with
-// v_mfma_i32_16x16x64_i8, twice (128 channels).  Rows of A are
-// (head, digit plane): q * scale_K of each head is held as a 22-bit
-// fixed-point integer split into three signed base-256 digits (row 4h + p,
-// p < 3; row 4h + 3 is zero), so the int32 accumulation is exact.  Columns
-// are tokens; B bytes are code bits, spread out of a packed word by
-// (w >> s) & 0x01010101, which yields channels 4s..4s+3 of the word's group
-// thanks to the interleaved packed layout.  Each lane ends up holding all
-// planes of one (head, token) score: s = (a0 + 256 a1 + 65536 a2) 2^-F + c0.
-// The first pass over the keys only gathers every head's min and max, which
-// fix g; the value pass reads the key tiles again (they are still in the
-// Infinity Cache) and recomputes the same scores, exactly, instead of keeping
-// 4 B per head and token on chip.
+// v_mfma_i32_16x16x64_i8, twice (128 channels).  B bytes are code bits left
+// in place in the packed word, one AND per register (bits_lo / bits_hi):
+// channel j's bit sits in its byte with weight 2^s(j), s(j) =
+// min(floor((j mod 32) / 4), 6).  Rows of A are (head, digit plane): each
+// head's q * scale_K is a 22-bit fixed-point integer Q (q' 2^F, rounded),
+// multiplied by 2^(7 - s(j)) for channel j and split into four signed
+// base-256 digits, so every product is 2^7 Q_j c_j and the int32 plane sums
+// are exact.  Columns are tokens.  Each lane ends up holding all planes of
+// one (head, token) score: s = ((a0 + 2^8 a1) + 2^16 (a2 + 2^8 a3)) 2^-(F+7)
+// + c0, the two halves exact in int32 and their sum rounded to float the same
+// way in both passes.  The first pass over the keys only gathers every
+// head's min and max, which fix g; the value pass reads the key tiles again
+// (they are still in the Infinity Cache) and recomputes the same scores,
+// instead of keeping 4 B per head and token on chip.
 //
 // V side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16], rows again
-// (head, plane), columns channels, contraction over tokens.  p = exp(g(s) -
-// max) in (0, 1] becomes P = round(p 2^22); its three bytes, the low two
-// offset by -128 (xor 0x80) so that they are valid int8, are the digit
-// planes.  Row 4h + 3 is all ones and counts the set code bits, which
-// restores the -128 offsets.  A lane produces the digits of 8 consecutive
-// tokens of one head, so one LDS write / read pair per wave hands them to the
-// lanes that feed A, already in the byte order of the packed V words.  The
-// planes combine into the exact integer sum_i P_i c_i, and the normalizer is
-// sum_i P_i (the same weights), both summed exactly: the result does not
-// depend on which wave took which tile.
+// (head, plane), columns channels, contraction over tokens; B is the masked
+// V word as on the K side.  p = exp(g(s) - max) in (0, 1] becomes
+// P = round(p 2^22); token i's digits are those of P 2^(7 - s(i)), signed
+// base 256 (the bytes of x + 0x808080, the low three offset back by 128).
+// A lane produces the digits of 8 consecutive tokens of one head, so one LDS
+// write / read pair per wave (a 4 x 4 byte transpose in registers) hands
+// them to the lanes that feed A.  The planes combine into the exact integer
+// 2^7 sum_i P_i c_i, and the normalizer is sum_i P_i (the same weights),
+// both summed exactly: the result does not depend on which wave took which
+// tile.
 //
 // The text tail (float K/V) is handled in plain float32 arithmetic.
 #include "cq_device.h"
@@ -117,7 +119,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // V-side A digits: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
+  __shared__ float s_lam[4], s_mu[4], s_ptail[4];
   __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
   __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
@@ -606,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][TB / 4];   // V-side A digits: [head][plane][TB bytes]
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWaves][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_tmax[4], s_ptail[4];
+  __shared__ float s_lam[4], s_mu[4], s_ptail[4];
   __shared__ float s_tailred[kThreads / 64][4][128];
   __shared__ float s_vred[kWaves][4][128];
   __shared__ float s_psum[kWaves][4];
