@@ -17,12 +17,15 @@ sample of the same workload (the ``cpu_baseline`` leg; the only place this
 file touches the oracle).
 
 Sweeps (not the headline line; one JSON line per point, then a table):
-    --sweeps               bit-width sweep (b = 1, 2, 4, 8 and the fp16
-                           baseline at B=32, n=3328, one layer) and the
-                           memory-budget sweep (32-layer stacks at the
-                           largest batch that fits 5/10/20/30 GiB of KV cache
-                           at 1 bit and at fp16, n = 3328 and 8192, one full
-                           decode step over all layers)
+    --sweeps [NAME ...]    bits: the bit-width sweep (b = 1, 2, 4, 8 and the
+                           fp16 baseline at B=32, n=3328, one layer);
+                           budget: the memory-budget sweep (32-layer stacks at
+                           the largest batch that fits 5/10/20/30 GiB of KV
+                           cache at 1 bit and at fp16, n = 3328 and 8192, one
+                           full decode step over all layers);
+                           graph: one 32-layer decode step issued layer by
+                           layer and replayed as one captured HIP graph
+                           (B=16 n=3328, B=64 n=8192).  No name: all three
 
 Profiling helpers (used to produce profiles/):
     --only {step,copy}     run only the timed steps, or only a 1 GiB copy
@@ -369,91 +372,133 @@ def sweeps(args):
         rows.append(row)
         print(json.dumps(row), flush=True)
 
-    # -- bit-width sweep: one layer, B=32, n=3328, decode with the Infinity Cache flushed
-    scratch = Flush(dev)
-    base = CONFIGS["bits_sweep_b1"]
-    K = kv_torch(base.seed, 0, ROLE_K, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
-    V = kv_torch(base.seed, 0, ROLE_V, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
-    kt = kv_torch(base.seed, 0, ROLE_KTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
-    vt = kv_torch(base.seed, 0, ROLE_VTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
-    q = q_torch(base.seed, 0, base.B, base.Hq, base.d, base.dtype, dev)
-    out = torch.empty((base.B, base.Hq, base.d), dtype=torch.float16, device=dev)
-    for bits in (1, 2, 4, 8):
-        cfg = CONFIGS[f"bits_sweep_b{bits}"]
-        note(f"bit sweep b={bits}")
-        kc, ks, km = cqb.cq_quantize_kv(K, bits, cqb.CQ_LAYOUT_K)
-        vc, vs, vm = cqb.cq_quantize_kv(V, bits, cqb.CQ_LAYOUT_V)
-        ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d, bits)),
-                         dtype=torch.uint8, device=dev)
-        t = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=bits, sm_scale=sm,
-                                             calib=cfg.calib, out=out, workspace=ws), args.steps, scratch)
-        nb = decode_bytes(cfg)
-        emit({"sweep": "bits", "bits": bits, "B": cfg.B, "n": cfg.n, "T": cfg.T, "calib": cfg.calib is not None,
-              "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(cfg.B / t, 1),
-              "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
-        del kc, ks, km, vc, vs, vm, ws
-    Kf, Vf = torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)
-    fws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(base.B, base.Hq, base.Hkv, base.n + base.T,
-                                                                   base.d)), dtype=torch.uint8, device=dev)
-    note("bit sweep fp16 baseline")
-    t = timed(lambda: cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=fws), args.steps, scratch)
-    nb = fp16_bytes(base)
-    emit({"sweep": "bits", "bits": 16, "B": base.B, "n": base.n, "T": base.T, "calib": False,
-          "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(base.B / t, 1),
-          "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
-    del K, V, kt, vt, q, out, Kf, Vf, fws, scratch
-    torch.cuda.empty_cache()
-
-    # -- memory-budget sweep: 32 layers, the largest batch whose cache fits the budget
+    which = set(args.sweeps) or {"bits", "budget", "graph"}
     layers, Hq, Hkv, d, T = 32, 32, 8, 128, 64
     calib = (0.9, 0.0, 0.8, 0.0)
-    for n in (3328, 8192):
-        for gib in (5, 10, 20, 30):
-            budget = gib << 30
-            for bits in (1, 0):
-                per_seq = cache_bytes_per_seq(n, T, Hkv, d, bits, layers)
-                B = budget // per_seq
-                note(f"budget {gib} GiB n={n} {'1-bit' if bits else 'fp16'}: batch {B}, building {layers} layers")
-                cache = []
-                for layer in range(layers):
-                    seed = 5
-                    K = kv_torch(seed, layer, ROLE_K, B, Hkv, n, d, "float16", dev)
-                    V = kv_torch(seed, layer, ROLE_V, B, Hkv, n, d, "float16", dev)
-                    kt = kv_torch(seed, layer, ROLE_KTAIL, B, Hkv, T, d, "float16", dev)
-                    vt = kv_torch(seed, layer, ROLE_VTAIL, B, Hkv, T, d, "float16", dev)
-                    q = q_torch(seed, layer, B, Hq, d, "float16", dev)
+
+    def bit_sweep():
+        """one layer, B=32, n=3328, decode with the Infinity Cache flushed"""
+        scratch = Flush(dev)
+        base = CONFIGS["bits_sweep_b1"]
+        K = kv_torch(base.seed, 0, ROLE_K, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+        V = kv_torch(base.seed, 0, ROLE_V, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+        kt = kv_torch(base.seed, 0, ROLE_KTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
+        vt = kv_torch(base.seed, 0, ROLE_VTAIL, base.B, base.Hkv, base.T, base.d, base.dtype, dev)
+        q = q_torch(base.seed, 0, base.B, base.Hq, base.d, base.dtype, dev)
+        out = torch.empty((base.B, base.Hq, base.d), dtype=torch.float16, device=dev)
+        for bits in (1, 2, 4, 8):
+            cfg = CONFIGS[f"bits_sweep_b{bits}"]
+            note(f"bit sweep b={bits}")
+            kc, ks, km = cqb.cq_quantize_kv(K, bits, cqb.CQ_LAYOUT_K)
+            vc, vs, vm = cqb.cq_quantize_kv(V, bits, cqb.CQ_LAYOUT_V)
+            ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d, bits)),
+                             dtype=torch.uint8, device=dev)
+            t = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=bits, sm_scale=sm,
+                                                 calib=cfg.calib, out=out, workspace=ws), args.steps, scratch)
+            nb = decode_bytes(cfg)
+            emit({"sweep": "bits", "bits": bits, "B": cfg.B, "n": cfg.n, "T": cfg.T, "calib": cfg.calib is not None,
+                  "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(cfg.B / t, 1),
+                  "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+            del kc, ks, km, vc, vs, vm, ws
+        Kf, Vf = torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)
+        fws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(base.B, base.Hq, base.Hkv, base.n + base.T,
+                                                                       base.d)), dtype=torch.uint8, device=dev)
+        note("bit sweep fp16 baseline")
+        t = timed(lambda: cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=fws), args.steps, scratch)
+        nb = fp16_bytes(base)
+        emit({"sweep": "bits", "bits": 16, "B": base.B, "n": base.n, "T": base.T, "calib": False,
+              "decode_ms": round(t * 1e3, 4), "seq_steps_per_s": round(base.B / t, 1),
+              "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+        del K, V, kt, vt, q, out, Kf, Vf, fws, scratch
+        torch.cuda.empty_cache()
+
+    def budget_sweep():
+        """32 layers, the largest batch whose cache fits the budget"""
+        for n in (3328, 8192):
+            for gib in (5, 10, 20, 30):
+                budget = gib << 30
+                for bits in (1, 0):
+                    per_seq = cache_bytes_per_seq(n, T, Hkv, d, bits, layers)
+                    B = budget // per_seq
+                    note(f"budget {gib} GiB n={n} {'1-bit' if bits else 'fp16'}: batch {B}, building {layers} layers")
+                    cache = []
+                    for layer in range(layers):
+                        seed = 5
+                        K = kv_torch(seed, layer, ROLE_K, B, Hkv, n, d, "float16", dev)
+                        V = kv_torch(seed, layer, ROLE_V, B, Hkv, n, d, "float16", dev)
+                        kt = kv_torch(seed, layer, ROLE_KTAIL, B, Hkv, T, d, "float16", dev)
+                        vt = kv_torch(seed, layer, ROLE_VTAIL, B, Hkv, T, d, "float16", dev)
+                        q = q_torch(seed, layer, B, Hq, d, "float16", dev)
+                        if bits:
+                            kc = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
+                            vc = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
+                            cache.append((q, kc, vc, kt, vt))
+                        else:
+                            cache.append((q, torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)))
+                        del K, V
+                    out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
                     if bits:
-                        kc = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
-                        vc = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
-                        cache.append((q, kc, vc, kt, vt))
+                        ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, 1)),
+                                         dtype=torch.uint8, device=dev)
+
+                        def step():
+                            for (q, (kc, ks, km), (vc, vs, vm), kt, vt) in cache:
+                                cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=1, sm_scale=sm,
+                                                   calib=calib, out=out, workspace=ws)
+                        nb = layers * B * Hkv * (2 * n * d // 8 + 2 * T * d * 2 + 4 * d * 4 + 2 * (Hq // Hkv) * d * 2)
                     else:
-                        cache.append((q, torch.cat([K, kt], dim=2), torch.cat([V, vt], dim=2)))
-                    del K, V
-                out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
-                if bits:
-                    ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, 1)),
-                                     dtype=torch.uint8, device=dev)
+                        ws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(B, Hq, Hkv, n + T, d)),
+                                         dtype=torch.uint8, device=dev)
 
-                    def step():
-                        for (q, (kc, ks, km), (vc, vs, vm), kt, vt) in cache:
-                            cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=1, sm_scale=sm,
-                                               calib=calib, out=out, workspace=ws)
-                    nb = layers * B * Hkv * (2 * n * d // 8 + 2 * T * d * 2 + 4 * d * 4 + 2 * (Hq // Hkv) * d * 2)
-                else:
-                    ws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(B, Hq, Hkv, n + T, d)),
-                                     dtype=torch.uint8, device=dev)
+                        def step():
+                            for (q, Kf, Vf) in cache:
+                                cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=ws)
+                        nb = layers * B * Hkv * (2 * (n + T) * d * 2 + 2 * (Hq // Hkv) * d * 2)
+                    t = timed(step, max(3, args.steps // 4))
+                    emit({"sweep": "budget", "budget_GiB": gib, "n": n, "T": T, "layers": layers,
+                          "cache": "1-bit" if bits else "fp16", "B": int(B), "step_ms": round(t * 1e3, 4),
+                          "seq_steps_per_s": round(B / t, 1), "GBs": round(nb / t / 1e9, 1),
+                          "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+                    del cache, out, ws
+                    torch.cuda.empty_cache()
 
-                    def step():
-                        for (q, Kf, Vf) in cache:
-                            cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=out, workspace=ws)
-                    nb = layers * B * Hkv * (2 * (n + T) * d * 2 + 2 * (Hq // Hkv) * d * 2)
-                t = timed(step, max(3, args.steps // 4))
-                emit({"sweep": "budget", "budget_GiB": gib, "n": n, "T": T, "layers": layers,
-                      "cache": "1-bit" if bits else "fp16", "B": int(B), "step_ms": round(t * 1e3, 4),
-                      "seq_steps_per_s": round(B / t, 1), "GBs": round(nb / t / 1e9, 1),
+    def graph_sweep():
+        """a 32-layer decode step, eager (one call per layer) and as one replayed HIP graph"""
+        from extreme_bit_kv_amd.attention import CalibQuantAttention, GraphedDecode, QuantizedVisualKV
+        for B, n in ((16, 3328), (64, 8192)):
+            note(f"graph: 32 layers B={B} n={n}")
+            attn = CalibQuantAttention(sm, calib)
+            stack, qs = [], []
+            for layer in range(layers):
+                K = kv_torch(6, layer, ROLE_K, B, Hkv, n, d, "float16", dev)
+                V = kv_torch(6, layer, ROLE_V, B, Hkv, n, d, "float16", dev)
+                stack.append((attn, QuantizedVisualKV(K, V, bits=1),
+                              kv_torch(6, layer, ROLE_KTAIL, B, Hkv, T, d, "float16", dev),
+                              kv_torch(6, layer, ROLE_VTAIL, B, Hkv, T, d, "float16", dev)))
+                qs.append(q_torch(6, layer, B, Hq, d, "float16", dev))
+                del K, V
+            outs = [torch.empty_like(q) for q in qs]
+
+            def eager():
+                for (a, c, kt, vt), q, o in zip(stack, qs, outs):
+                    a(q, c, kt, vt, out=o)
+            graphed = GraphedDecode(stack, qs)
+            te = timed(eager, args.steps)
+            tg = timed(graphed.step, args.steps)
+            nb = layers * B * Hkv * (2 * n * d // 8 + 2 * T * d * 2 + 4 * d * 4 + 2 * (Hq // Hkv) * d * 2)
+            for mode, t in (("eager", te), ("graph", tg)):
+                emit({"sweep": "graph", "mode": mode, "n": n, "T": T, "layers": layers, "B": B,
+                      "step_ms": round(t * 1e3, 4), "seq_steps_per_s": round(B / t, 1), "GBs": round(nb / t / 1e9, 1),
                       "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
-                del cache, out, ws
-                torch.cuda.empty_cache()
+            del stack, qs, outs, graphed
+            torch.cuda.empty_cache()
+
+    if "bits" in which:
+        bit_sweep()
+    if "budget" in which:
+        budget_sweep()
+    if "graph" in which:
+        graph_sweep()
 
     # table
     print("\n| sweep | point | B | ms | seq-steps/s | GB/s | of 8 TB/s |", file=sys.stderr)
@@ -461,6 +506,8 @@ def sweeps(args):
     for r in rows:
         if r["sweep"] == "bits":
             pt, ms = (f"b={r['bits']}" if r["bits"] < 16 else "fp16") + f", n={r['n']}", r["decode_ms"]
+        elif r["sweep"] == "graph":
+            pt, ms = f"{r['layers']} layers, n={r['n']}, {r['mode']}", r["step_ms"]
         else:
             pt, ms = f"{r['budget_GiB']} GiB, n={r['n']}, {r['cache']}", r["step_ms"]
         print(f"| {r['sweep']} | {pt} | {r['B']} | {ms} | {r['seq_steps_per_s']} | {r['GBs']} | {r['frac_8TBs']} |",
@@ -553,7 +600,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["step", "copy"], default=None)
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
-    ap.add_argument("--sweeps", action="store_true")
+    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph"], default=None)
     ap.add_argument("--command-note", default="")
     args = ap.parse_args()
     if args.summarize:
@@ -564,7 +611,7 @@ def main():
         print("bench.py measures one GPU only: the path shards by batch or kv head with no "
               "communication, and no multi-GPU figure is produced. Use --gpus 1.", file=sys.stderr)
         sys.exit(2)
-    if args.sweeps:
+    if args.sweeps is not None:
         sweeps(args)
         return
     run(args)
