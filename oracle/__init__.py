@@ -11,9 +11,11 @@ their stored scale (no page prints them).
 """
 from .cq_oracle import (Calib, attend_dense, calibrate_rows, dense_scores, code_bit_offset, decode_attn,
                         decode_unit, decode_unit_postscaled, dequant, exact_ints, nearest_f32,
-                        pack, quantize, quantize_unit, unpack, visual_scores)
-from .brute import decode_brute, quantize_brute
+                        pack, quantize, quantize_unit, quantize_with_range, range_update, unpack,
+                        visual_scores)
+from .brute import decode_brute, quantize_brute, quantize_brute_range
 
 __all__ = ["Calib", "attend_dense", "calibrate_rows", "dense_scores", "code_bit_offset", "decode_attn",
            "decode_unit", "decode_unit_postscaled", "dequant", "exact_ints", "nearest_f32",
-           "pack", "quantize", "quantize_unit", "unpack", "visual_scores", "decode_brute", "quantize_brute"]
+           "pack", "quantize", "quantize_unit", "quantize_with_range", "range_update", "unpack", "visual_scores",
+           "decode_brute", "quantize_brute", "quantize_brute_range"]

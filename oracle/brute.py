@@ -40,6 +40,30 @@ def quantize_brute(x, bits):
     return codes, mn, mx
 
 
+def quantize_brute_range(x, mn, mx, bits):
+    """Codes of x (n rows of d Python floats) on a given range: codes[i][j] is
+    the index k in 0..L of the level mn_j + k (mx_j - mn_j)/L nearest to
+    x[i][j] (exact arithmetic, ties to even k), 0 when mx_j <= mn_j.  Values
+    outside the range simply find an end level nearest."""
+    L = (1 << bits) - 1
+    n, d = len(x), len(x[0])
+    codes = [[0] * d for _ in range(n)]
+    for j in range(d):
+        lo, hi = Fraction(mn[j]), Fraction(mx[j])
+        if hi <= lo:
+            continue
+        step = (hi - lo) / L
+        for i in range(n):
+            v = Fraction(x[i][j])
+            best_k, best_err = None, None
+            for k in range(L + 1):
+                err = abs(v - (lo + k * step))
+                if best_err is None or err < best_err or (err == best_err and k % 2 == 0):
+                    best_k, best_err = k, err
+            codes[i][j] = best_k
+    return codes
+
+
 def decode_brute(q, Khat, Vhat, Kt, Vt, sm_scale, calib):
     """q: G lists of d; Khat/Vhat: n lists of d (already dequantized); Kt/Vt: T lists.
 

@@ -141,6 +141,97 @@ def quantize_unit(x: np.ndarray, bits: int):
     return codes, scale, minv, scale_exact
 
 
+# --------------------------------------------------------------------------
+# Chunked prefill: the range gathered chunk by chunk, codes on a given range
+# ([ART] Method part 1 applied to a visual segment that arrives in pieces)
+# --------------------------------------------------------------------------
+
+def range_update(mn, mx, x_chunk: np.ndarray, reset: bool):
+    """Merge one chunk x_chunk[m, d] (m >= 1) of a unit's visual tokens into
+    the running per-channel range (mn, mx), float32 [d].
+
+    Reading: the range of [ART] Method part 1 is the per-channel minimum and
+    maximum over the unit's tokens.  Minimum and maximum are associative, so
+    a segment that arrives in chunks has, after its last chunk, exactly the
+    range of the whole segment.  ``reset`` starts a new range from the chunk
+    (mn and mx are then ignored).
+
+    Returns (mn', mx', grew): grew is True when some channel's range became
+    wider than (mn, mx) (always True under reset).
+    """
+    c = np.asarray(x_chunk)
+    if c.ndim != 2 or c.shape[0] < 1:
+        raise ValueError("a chunk is [m, d] with m >= 1")
+    cmn = c.min(axis=0).astype(np.float32)
+    cmx = c.max(axis=0).astype(np.float32)
+    if reset:
+        return cmn, cmx, True
+    mn = np.asarray(mn, np.float32)
+    mx = np.asarray(mx, np.float32)
+    nmn = np.minimum(mn, cmn)
+    nmx = np.maximum(mx, cmx)
+    grew = bool(np.any(nmn < mn) or np.any(nmx > mx))
+    return nmn, nmx, grew
+
+
+def _exact_common(x: np.ndarray, mn: np.ndarray, mx: np.ndarray):
+    """(X, MN, MX, k): x == X 2^-k, mn == MN 2^-k, mx == MX 2^-k exactly."""
+    on_f16_grid = (x.dtype == np.float16 and
+                   all(np.all(np.abs(v) <= 65504) and np.all(v.astype(np.float64) * 2.0 ** 24 ==
+                                                          np.round(v.astype(np.float64) * 2.0 ** 24))
+                       for v in (mn, mx)))
+    if on_f16_grid:
+        X, k = exact_ints(x)
+        to = lambda v: (v.astype(np.float64) * 2.0 ** 24).astype(np.int64)   # noqa: E731
+        return X, to(mn), to(mx), k
+    X, k = exact_ints(x.astype(np.float32))           # float16 -> float32 is exact
+    MN, _ = exact_ints(mn)
+    MX, _ = exact_ints(mx)
+    return X, MN, MX, k
+
+
+def quantize_with_range(x: np.ndarray, mn, mx, bits: int):
+    """Codes of one unit's block x[n, d] on the grid of a GIVEN per-channel
+    range [mn, mx] (float32 [d]), for a chunked prefill in which the range is
+    gathered before (or while) the codes are written.
+
+    [ART] Method part 1's quantizer, with its range supplied instead of
+    measured on x: code = round-half-to-even((x - mn) L / (mx - mn)), decided
+    exactly, L = 2**b - 1.
+
+    Readings:
+      * a value outside [mn, mx] takes the nearest level, i.e. its code is
+        clamped to [0, L] (with mn, mx the range of x itself no value is
+        outside and this is ``quantize_unit``);
+      * a channel with mx <= mn gets code 0 and scale 0;
+      * stored parameters as in ``quantize_unit``: scale = (mx - mn)/L rounded
+        to the nearest float32, min = mn.
+
+    Returns (codes int64 [n, d], scale float32 [d], minv float32 [d]).
+    """
+    if bits not in (1, 2, 4, 8):
+        raise ValueError("bits must be 1, 2, 4 or 8")
+    x = np.asarray(x)
+    mn = np.asarray(mn, np.float32)
+    mx = np.asarray(mx, np.float32)
+    n, d = x.shape
+    L = (1 << bits) - 1
+    X, MN, MX, k = _exact_common(x, mn, mx)
+    den = MX - MN
+    live = den > 0
+    den_safe = np.where(live, den, 1)
+    num = (X - MN) * L
+    q = num // den_safe                                   # floor, also for negative num
+    r = num - q * den_safe                                # 0 <= r < den
+    up = (2 * r > den_safe) | ((2 * r == den_safe) & (q % 2 != 0))
+    codes = np.clip(np.where(live, q + up, 0).astype(np.int64), 0, L)
+    scale = np.zeros(d, np.float32)
+    for j in range(d):
+        if live[j]:
+            scale[j] = nearest_f32(Fraction(int(den[j]), L << k))
+    return codes.reshape(n, d), scale, mn.copy()
+
+
 def dequant(codes: np.ndarray, scale: np.ndarray, minv: np.ndarray) -> np.ndarray:
     """x_hat = min + code * scale, per channel ([ART] Method part 2)."""
     return np.asarray(minv, np.float64) + np.asarray(codes, np.float64) * np.asarray(scale, np.float64)
