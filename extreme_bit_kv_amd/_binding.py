@@ -33,7 +33,8 @@ CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLI
 
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
-            "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16")
+            "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16", "cq_kv_range_update",
+            "cq_quantize_kv_rows")
 
 
 class cq_calib(ctypes.Structure):
@@ -58,6 +59,10 @@ lib.cq_quantize_kv_workspace.argtypes = [_i32] * 5
 lib.cq_quantize_kv.restype = _i32
 lib.cq_quantize_kv.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                                ctypes.POINTER(cq_opts), _vp]
+lib.cq_kv_range_update.restype = _i32
+lib.cq_kv_range_update.argtypes = [_vp, _i32] + [_i32] * 6 + [_vp, _vp, _i32, _vp, _vp]
+lib.cq_quantize_kv_rows.restype = _i32
+lib.cq_quantize_kv_rows.argtypes = [_vp, _i32] + [_i32] * 8 + [_vp, _vp, _vp, _i32, _vp, _vp, _vp, _vp]
 lib.cq_decode_attn_workspace.restype = _sz
 lib.cq_decode_attn_workspace.argtypes = [_i32] * 7
 lib.cq_decode_attn.restype = _i32
@@ -274,3 +279,68 @@ def cq_decode_attn_fp16(q, k, v, sm_scale: float, out=None, workspace=None):
                                  _stream(q.device))
     _check(st, "cq_decode_attn_fp16")
     return out
+
+
+def _rows_ptr(x, row0: int, t0: int, m: int):
+    """Pointer to row row0 of every (b, h) of x [B, H, x_rows, d]: the segment
+    starts there, the unit stride stays x_rows rows."""
+    B, H, x_rows, d = x.shape
+    if row0 < 0 or t0 < 0 or m < 0 or row0 + t0 + m > x_rows:
+        raise ValueError(f"rows [{row0 + t0}, {row0 + t0 + m}) are not inside x's {x_rows} rows")
+    return ctypes.c_void_p(x.data_ptr() + row0 * d * x.element_size())
+
+
+def cq_kv_range_update(x, t0: int, m: int, mn=None, mx=None, *, reset: bool, grew=None, row0: int = 0):
+    """Merge rows [row0 + t0, row0 + t0 + m) of x [B, H, x_rows, d]
+    (float16/float32) into the running per-channel range mn, mx (float32
+    [B, H, d], updated in place; allocated when reset and not given).  grew
+    (uint32 as int32 [B, H]), if given, is set to 1 where a channel's range
+    became wider.  Returns (mn, mx)."""
+    torch = _torch()
+    _need(x, "x")
+    B, H, x_rows, d = x.shape
+    dev = x.device
+    xp = _rows_ptr(x, row0, t0, m)
+    if mn is None or mx is None:
+        if not reset:
+            raise ValueError("mn and mx are required unless reset")
+        mn = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+        mx = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _need(mn, "mn", (B, H, d), torch.float32, dev)
+    _need(mx, "mx", (B, H, d), torch.float32, dev)
+    if grew is not None:
+        _need(grew, "grew", (B, H), torch.int32, dev)
+    st = lib.cq_kv_range_update(xp, _dtype_code(x), B, H, x_rows, t0, m, d, _ptr(mn), _ptr(mx), int(reset),
+                                _ptr(grew), _stream(dev))
+    _check(st, "cq_kv_range_update")
+    return mn, mx
+
+
+def cq_quantize_kv_rows(x, t0: int, m: int, bits: int, layout: int, mn, mx, n: int, codes=None, scale=None,
+                        minv=None, unit_mask=None, row0: int = 0):
+    """Codes of tokens [t0, t0 + m) of the segment that starts at row row0 of
+    x [B, H, x_rows, d], on the given range mn, mx (float32 [B, H, d]), into
+    code words laid out for n tokens (allocated when not given).  unit_mask
+    (int32 [B, H]) skips the units where it is 0.  Returns (codes, scale,
+    minv)."""
+    torch = _torch()
+    _need(x, "x")
+    B, H, x_rows, d = x.shape
+    dev = x.device
+    xp = _rows_ptr(x, row0, t0, m)
+    shape = code_words_shape(B, H, n, d, bits, layout)
+    if codes is None:
+        codes = torch.zeros(shape, dtype=torch.int32, device=dev)
+    if scale is None:
+        scale = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    if minv is None:
+        minv = torch.empty((B, H, d), dtype=torch.float32, device=dev)
+    _need(codes, "codes", shape, torch.int32, dev)
+    for name, t in (("mn", mn), ("mx", mx), ("scale", scale), ("minv", minv)):
+        _need(t, name, (B, H, d), torch.float32, dev)
+    if unit_mask is not None:
+        _need(unit_mask, "unit_mask", (B, H), torch.int32, dev)
+    st = lib.cq_quantize_kv_rows(xp, _dtype_code(x), B, H, x_rows, t0, m, d, bits, layout, _ptr(mn), _ptr(mx),
+                                 _ptr(unit_mask), n, _ptr(codes), _ptr(scale), _ptr(minv), _stream(dev))
+    _check(st, "cq_quantize_kv_rows")
+    return codes, scale, minv

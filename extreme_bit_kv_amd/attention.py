@@ -33,13 +33,25 @@ class QuantizedVisualKV:
     packed codes and the per-channel scale and minimum replace them; the
     full-precision tensors can be freed afterwards."""
 
-    def __init__(self, k_visual: torch.Tensor, v_visual: torch.Tensor, bits: int = 1):
+    def __init__(self, k_visual: Optional[torch.Tensor], v_visual: Optional[torch.Tensor], bits: int = 1):
+        self.bits = bits
+        if k_visual is None and v_visual is None:                 # filled by from_codes
+            return
         if k_visual.shape != v_visual.shape:
             raise ValueError(f"K {tuple(k_visual.shape)} and V {tuple(v_visual.shape)} differ")
         self.B, self.Hkv, self.n, self.d = k_visual.shape
-        self.bits = bits
         self.k = cq_quantize_kv(k_visual, bits, CQ_LAYOUT_K)      # (codes, scale, min)
         self.v = cq_quantize_kv(v_visual, bits, CQ_LAYOUT_V)
+
+    @classmethod
+    def from_codes(cls, k, v, n: int, bits: int) -> "QuantizedVisualKV":
+        """Wrap codes made elsewhere (e.g. by a chunked prefill): k and v are
+        (codes, scale, min) in the K and V layouts for n tokens."""
+        self = cls(None, None, bits)
+        self.B, self.Hkv, self.d = k[1].shape
+        self.n = n
+        self.k, self.v = tuple(k), tuple(v)
+        return self
 
     @property
     def nbytes(self) -> int:

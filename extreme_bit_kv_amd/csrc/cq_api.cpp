@@ -94,6 +94,48 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
 }
 
 // ---------------------------------------------------------------------------
+cq_status cq_kv_range_update(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, int32_t x_rows, int32_t t0,
+                             int32_t m, int32_t d, float* mn, float* mx, int32_t reset, uint32_t* grew,
+                             void* stream) {
+  if (!fits(B, H, x_rows, d) || d <= 0 || !valid_dtype(x_dtype) || t0 < 0 || m < 0 ||
+      (int64_t)t0 + m > x_rows || (reset != 0 && reset != 1))
+    return CQ_ERR_INVALID_ARG;
+  if (reset && m == 0) return CQ_ERR_INVALID_ARG;                 // a range needs a row
+  const int64_t units = (int64_t)B * H;
+  if (units > 0) {
+    if (mn == nullptr || mx == nullptr || (m > 0 && x == nullptr)) return CQ_ERR_INVALID_ARG;
+    if (!al16(x) || !al4(mn) || !al4(mx) || !al4(grew)) return CQ_ERR_INVALID_ARG;
+  }
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  cqi::RowsArgs a{x, x_dtype, B, H, (long)x_rows, t0, m, d, (hipStream_t)stream};
+  clear_stale_hip_error();
+  return from_hip(cqi::range_update(a, mn, mx, reset, grew));
+}
+
+cq_status cq_quantize_kv_rows(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, int32_t x_rows, int32_t t0,
+                              int32_t m, int32_t d, int32_t bits, cq_layout layout, const float* mn, const float* mx,
+                              const uint32_t* unit_mask, int32_t n, uint32_t* codes, float* scale, float* minv,
+                              void* stream) {
+  if (!fits(B, H, x_rows, d) || !fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype) ||
+      (layout != CQ_LAYOUT_K && layout != CQ_LAYOUT_V))
+    return CQ_ERR_INVALID_ARG;
+  if ((d * bits) % 32 != 0 || t0 < 0 || m < 0 || (int64_t)t0 + m > n || (int64_t)t0 + m > x_rows)
+    return CQ_ERR_INVALID_ARG;
+  if (t0 % 32 != 0 || (m % 32 != 0 && t0 + m != n)) return CQ_ERR_INVALID_ARG;   // whole V words per call
+  const int64_t units = (int64_t)B * H;
+  if (units > 0 && m > 0) {
+    if (x == nullptr || codes == nullptr || mn == nullptr || mx == nullptr || scale == nullptr || minv == nullptr)
+      return CQ_ERR_INVALID_ARG;
+    if (!al16(x) || !al16(codes) || !al4(mn) || !al4(mx) || !al4(unit_mask) || !al4(scale) || !al4(minv))
+      return CQ_ERR_INVALID_ARG;
+  }
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  cqi::RowsArgs a{x, x_dtype, B, H, (long)x_rows, t0, m, d, (hipStream_t)stream};
+  clear_stale_hip_error();
+  return from_hip(cqi::quant_rows(a, bits, layout, mn, mx, unit_mask, n, codes, scale, minv));
+}
+
+// ---------------------------------------------------------------------------
 size_t cq_decode_attn_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t T, int32_t d,
                                 int32_t bits) {
   if (!fits(B, Hq, n, d) || !fits(B, Hkv, T, d) || Hkv <= 0 || Hq % Hkv != 0 || !valid_bits(bits)) return 0;

@@ -40,6 +40,21 @@ size_t quant_fused_ws(int B, int H, int n, int d);
 bool quant_fused_supported(const QuantArgs& a);
 hipError_t quant_fused(const QuantArgs& a);
 
+// ---- chunked prefill: range update and row quantization ----------------
+struct RowsArgs {
+  const void* x;        // [B][H][x_rows][d]
+  int dtype;            // cq_dtype
+  int B, H;
+  long x_rows;
+  int t0, m, d;         // rows [t0, t0 + m) of every (b, h)
+  hipStream_t stream;
+};
+hipError_t range_update(const RowsArgs& a, float* mn, float* mx, int reset, uint32_t* grew);
+hipError_t quant_rows(const RowsArgs& a, int bits, int layout, const float* mn, const float* mx,
+                      const uint32_t* unit_mask, int n_codes, uint32_t* codes, float* scale, float* minv);
+hipError_t quant_rows_generic(const RowsArgs& a, int bits, int layout, const float* mn, const float* mx,
+                              const uint32_t* unit_mask, int n_codes, uint32_t* codes, float* scale, float* minv);
+
 // ---- decode -------------------------------------------------------------
 struct DecodeArgs {
   const void* q;

@@ -154,7 +154,45 @@ __global__ void qz_params(const float2* __restrict__ part, int chunks, int d, in
 __device__ __forceinline__ int code_of(float x, const QParams& p, int L) {
   if (!(p.inv > 0.0)) return 0;
   const double t = ((double)x - (double)p.mn) * p.inv;
+  if (t <= -1.0) return 0;                      // far outside a given range: an end level
+  if (t >= L + 1.0) return L;
   return cqd::exact_code(x, p.mn, p.mx, t, L, 0x1p-30);
+}
+
+// Rows coded by one pack launch: tokens [t_first, n_end) of every unit; x has
+// x_rows rows per unit, the code words are laid out for n_codes tokens.
+struct Rows {
+  long x_rows;
+  int t_first, n_end, n_codes;
+};
+
+// The unit's channel parameters into LDS: from the workspace (one-shot path)
+// or from a given range (row path; tile 0 then stores scale and minimum).
+__device__ __forceinline__ void load_params(QParams* sp, const QParams* __restrict__ prm, const float* __restrict__ mn,
+                                            const float* __restrict__ mx, int unit, int L, float* __restrict__ scale,
+                                            float* __restrict__ minv) {
+  if (threadIdx.x >= kD) return;
+  const size_t o = (size_t)unit * kD + threadIdx.x;
+  if (prm != nullptr) {
+    sp[threadIdx.x] = prm[o];
+    return;
+  }
+  QParams p;
+  p.mn = mn[o];
+  p.mx = mx[o];
+  p.inv = 0.0;
+  float sc = 0.0f;
+  if (p.mx > p.mn) {
+    double rh, rl;
+    cqd::two_sum((double)p.mx, -(double)p.mn, rh, rl);
+    p.inv = (double)L / (rh + rl);
+    sc = scale_rn(p.mn, p.mx, L);
+  }
+  sp[threadIdx.x] = p;
+  if (blockIdx.x == 0) {
+    scale[o] = sc;
+    minv[o] = p.mn;
+  }
 }
 
 // K layout: a block packs kTok tokens.  Words are computed with the word
@@ -162,21 +200,26 @@ __device__ __forceinline__ int code_of(float x, const QParams& p, int L) {
 // written plane by plane (kTok consecutive words of a plane per wave).
 constexpr int kTok = 64;
 template <typename T, int BITS>
-__global__ void __launch_bounds__(kThreads) qz_pack_k(const T* __restrict__ x, int n,
-                                                      const QParams* __restrict__ prm,
-                                                      uint32_t* __restrict__ codes) {
+__global__ void __launch_bounds__(kThreads) qz_pack_k(const T* __restrict__ x, Rows g,
+                                                      const QParams* __restrict__ prm, const float* __restrict__ mn,
+                                                      const float* __restrict__ mx,
+                                                      const uint32_t* __restrict__ unit_mask,
+                                                      uint32_t* __restrict__ codes, float* __restrict__ scale,
+                                                      float* __restrict__ minv) {
   constexpr int E = 32 / BITS, W = kD / E, L = (1 << BITS) - 1;
-  const int unit = blockIdx.y, i0 = blockIdx.x * kTok;
+  const int unit = blockIdx.y, i0 = g.t_first + blockIdx.x * kTok;
+  if (unit_mask != nullptr && unit_mask[unit] == 0u) return;
+  const int n = g.n_end;
   __shared__ QParams sp[kD];                     // the unit's channel parameters
   __shared__ uint32_t sw[W][kTok + 1];
-  if (threadIdx.x < kD) sp[threadIdx.x] = prm[(size_t)unit * kD + threadIdx.x];
+  load_params(sp, prm, mn, mx, unit, L, scale, minv);
   __syncthreads();
   for (int q = threadIdx.x; q < kTok * W; q += kThreads) {
     const int w = q % W, ti = q / W, i = i0 + ti;
     uint32_t word = 0;
     if (i < n) {
       float v[E];
-      load_vals<T, E>(x + ((size_t)unit * n + i) * kD + w * E, v);
+      load_vals<T, E>(x + ((size_t)unit * g.x_rows + i) * kD + w * E, v);
 #pragma unroll
       for (int e = 0; e < E; ++e) word |= (uint32_t)code_of(v[e], sp[w * E + e], L) << cqd::code_off(e, BITS);
     }
@@ -185,26 +228,31 @@ __global__ void __launch_bounds__(kThreads) qz_pack_k(const T* __restrict__ x, i
   __syncthreads();
   for (int q = threadIdx.x; q < kTok * W; q += kThreads) {
     const int w = q / kTok, ti = q % kTok, i = i0 + ti;
-    if (i < n) codes[((size_t)unit * W + w) * n + i] = sw[w][ti];
+    if (i < n) codes[((size_t)unit * W + w) * g.n_codes + i] = sw[w][ti];
   }
 }
 
 // V layout: thread (r, cg) packs the words (r, 8 cg .. 8 cg + 7): per token of
 // the row it reads 16 bytes (8 channels) and stores two 16-byte word groups.
 template <typename T, int BITS>
-__global__ void __launch_bounds__(kThreads) qz_pack_v(const T* __restrict__ x, int n,
-                                                      const QParams* __restrict__ prm,
-                                                      uint32_t* __restrict__ codes) {
+__global__ void __launch_bounds__(kThreads) qz_pack_v(const T* __restrict__ x, Rows g,
+                                                      const QParams* __restrict__ prm, const float* __restrict__ mn,
+                                                      const float* __restrict__ mx,
+                                                      const uint32_t* __restrict__ unit_mask,
+                                                      uint32_t* __restrict__ codes, float* __restrict__ scale,
+                                                      float* __restrict__ minv) {
   constexpr int E = 32 / BITS, L = (1 << BITS) - 1;
   const int unit = blockIdx.y;
-  const int R = (n + E - 1) / E;
+  if (unit_mask != nullptr && unit_mask[unit] == 0u) return;
+  const int n = g.n_end;
+  const int r_first = g.t_first / E, R_end = (n + E - 1) / E, R = (g.n_codes + E - 1) / E;
   __shared__ QParams sp[kD];
-  if (threadIdx.x < kD) sp[threadIdx.x] = prm[(size_t)unit * kD + threadIdx.x];
+  load_params(sp, prm, mn, mx, unit, L, scale, minv);
   __syncthreads();
   const long idx = (long)blockIdx.x * kThreads + threadIdx.x;
-  if (idx >= (long)R * (kD / 8)) return;
-  const int r = (int)(idx / (kD / 8)), cg = (int)(idx % (kD / 8));
-  const T* xu = x + (size_t)unit * n * kD + 8 * cg;
+  if (idx >= (long)(R_end - r_first) * (kD / 8)) return;
+  const int r = r_first + (int)(idx / (kD / 8)), cg = (int)(idx % (kD / 8));
+  const T* xu = x + (size_t)unit * g.x_rows * kD + 8 * cg;
   uint32_t word[8] = {0u, 0u, 0u, 0u, 0u, 0u, 0u, 0u};
 #pragma unroll 4
   for (int e = 0; e < E; ++e) {
@@ -231,17 +279,31 @@ __global__ void qz_zero(float* scale, float* minv, long count) {
 }
 
 template <typename T, int BITS>
-hipError_t pack(const cqi::QuantArgs& a, const T* x, const QParams* prm, int units) {
+hipError_t pack(int layout, const T* x, Rows g, const QParams* prm, const float* mn, const float* mx,
+                const uint32_t* unit_mask, uint32_t* codes, float* scale, float* minv, int units, hipStream_t st) {
   constexpr int E = 32 / BITS;
-  if (a.layout == CQ_LAYOUT_K) {
-    CQ_LAUNCH((qz_pack_k<T, BITS>), dim3((unsigned)((a.n + kTok - 1) / kTok), units), dim3(kThreads), 0,
-              a.stream, x, a.n, prm, a.codes);
+  const int m = g.n_end - g.t_first;
+  if (layout == CQ_LAYOUT_K) {
+    CQ_LAUNCH((qz_pack_k<T, BITS>), dim3((unsigned)((m + kTok - 1) / kTok), units), dim3(kThreads), 0, st, x, g, prm,
+              mn, mx, unit_mask, codes, scale, minv);
   } else {
-    const long threads = (long)((a.n + E - 1) / E) * (kD / 8);
+    const long threads = (long)((g.n_end + E - 1) / E - g.t_first / E) * (kD / 8);
     CQ_LAUNCH((qz_pack_v<T, BITS>), dim3((unsigned)((threads + kThreads - 1) / kThreads), units), dim3(kThreads),
-              0, a.stream, x, a.n, prm, a.codes);
+              0, st, x, g, prm, mn, mx, unit_mask, codes, scale, minv);
   }
   return hipSuccess;
+}
+
+template <typename T>
+hipError_t pack_bits(int bits, int layout, const T* x, Rows g, const QParams* prm, const float* mn, const float* mx,
+                     const uint32_t* unit_mask, uint32_t* codes, float* scale, float* minv, int units,
+                     hipStream_t st) {
+  switch (bits) {
+    case 1: return pack<T, 1>(layout, x, g, prm, mn, mx, unit_mask, codes, scale, minv, units, st);
+    case 2: return pack<T, 2>(layout, x, g, prm, mn, mx, unit_mask, codes, scale, minv, units, st);
+    case 4: return pack<T, 4>(layout, x, g, prm, mn, mx, unit_mask, codes, scale, minv, units, st);
+    default: return pack<T, 8>(layout, x, g, prm, mn, mx, unit_mask, codes, scale, minv, units, st);
+  }
 }
 
 template <typename T>
@@ -261,12 +323,9 @@ hipError_t run(const cqi::QuantArgs& a) {
   CQ_LAUNCH(qz_stats<T>, dim3(chunks, units), dim3(kThreads), 0, a.stream, x, a.n, chunks, part);
   CQ_LAUNCH(qz_params, dim3(units), dim3(a.d), 0, a.stream, part, chunks, a.d, a.bits, a.scale, a.minv,
                      prm);
-  switch (a.bits) {
-    case 1: return pack<T, 1>(a, x, prm, units);
-    case 2: return pack<T, 2>(a, x, prm, units);
-    case 4: return pack<T, 4>(a, x, prm, units);
-    default: return pack<T, 8>(a, x, prm, units);
-  }
+  const Rows g{(long)a.n, 0, a.n, a.n};
+  return pack_bits<T>(a.bits, a.layout, x, g, prm, nullptr, nullptr, nullptr, a.codes, nullptr, nullptr, units,
+                      a.stream);
 }
 
 }  // namespace
@@ -281,6 +340,18 @@ size_t quant_generic_ws(int B, int H, int n, int d) {
 
 hipError_t quant_generic(const QuantArgs& a) {
   return a.dtype == CQ_F16 ? run<__half>(a) : run<float>(a);
+}
+
+hipError_t quant_rows_generic(const RowsArgs& a, int bits, int layout, const float* mn, const float* mx,
+                              const uint32_t* unit_mask, int n_codes, uint32_t* codes, float* scale, float* minv) {
+  const int units = a.B * a.H;
+  if (units == 0 || a.m == 0) return hipSuccess;
+  const Rows g{a.x_rows, a.t0, a.t0 + a.m, n_codes};
+  if (a.dtype == CQ_F16)
+    return pack_bits<__half>(bits, layout, (const __half*)a.x, g, nullptr, mn, mx, unit_mask, codes, scale, minv,
+                             units, a.stream);
+  return pack_bits<float>(bits, layout, (const float*)a.x, g, nullptr, mn, mx, unit_mask, codes, scale, minv, units,
+                          a.stream);
 }
 
 }  // namespace cqi

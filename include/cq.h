@@ -156,6 +156,82 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype,
                          const cq_opts* opts, void* stream);
 
 /* ------------------------------------------------------------------------
+ * Chunked prefill: quantization of a visual segment that is written chunk by
+ * chunk (a chunked prefill, or video frames appended to the segment).
+ * [ART] Method part 1 takes the range per channel over the tokens of one
+ * head; minimum and maximum are associative, so the range merged over the
+ * chunks is the segment's range, and rows coded on it are exactly the codes
+ * cq_quantize_kv gives for the whole segment.  The two calls below need no
+ * workspace and no rendezvous between workgroups:
+ *
+ *   for each chunk [t, t + m) written to the float16/float32 cache x:
+ *       cq_kv_range_update(x, .., t0 = t, m, .., reset = (t == 0), grew)
+ *   once the segment [0, n) is complete:
+ *       cq_quantize_kv_rows(x, .., t0 = 0, m = n, .., n, codes, scale, minv)
+ *
+ * Codes may also be written as chunks arrive, on the range known so far;
+ * a later chunk that widens a unit's range (grew = 1) makes that unit's
+ * earlier codes stale, and they are written again with unit_mask = grew.
+ * ------------------------------------------------------------------------ */
+
+/* cq_kv_range_update — merge rows [t0, t0 + m) of every (b, h) into a running
+ * per-channel range.
+ *
+ *   x       device, [B][H][x_rows][d] of x_dtype (CQ_F16 or CQ_F32), finite
+ *           values; only rows [t0, t0 + m) are read (the cache being filled).
+ *           x may point at row s of every (b, h) of a larger cache of x_rows
+ *           rows per (b, h) (a segment that starts at row s), provided
+ *           s + t0 + m <= x_rows.
+ *   mn, mx  device, float32 [B][H][d], in/out: mn = min(mn, rows),
+ *           mx = max(mx, rows) per channel.  reset = 1 starts a new range from
+ *           the rows (the previous contents are ignored; m >= 1 required).
+ *           A zero is stored as +0.
+ *   grew    device, uint32 [B][H], or NULL: set to 1 where this call made some
+ *           channel's range strictly wider (always 1 under reset), else 0
+ *   Requires 0 <= t0, 0 <= m, t0 + m <= x_rows, d == 128 (else UNSUPPORTED).
+ *   m == 0 without reset only clears grew.  Calls on the same mn/mx must not
+ *   overlap (each call's result is exact whatever its own order of updates).
+ */
+cq_status cq_kv_range_update(const void* x, cq_dtype x_dtype,
+                             int32_t B, int32_t H, int32_t x_rows,
+                             int32_t t0, int32_t m, int32_t d,
+                             float* mn, float* mx, int32_t reset,
+                             uint32_t* grew, void* stream);
+
+/* cq_quantize_kv_rows — codes of rows [t0, t0 + m) of every (b, h) on a GIVEN
+ * per-channel range, written into a code buffer laid out for n tokens.
+ *
+ *   x         device, [B][H][x_rows][d] of x_dtype, finite values; may point
+ *             at row s of a larger cache as for cq_kv_range_update
+ *   bits, layout  as for cq_quantize_kv
+ *   mn, mx    device, float32 [B][H][d]: the range (e.g. from
+ *             cq_kv_range_update); a channel with mx <= mn gets code 0 and
+ *             scale 0
+ *   unit_mask device, uint32 [B][H], or NULL: units with mask 0 are skipped
+ *             (none of their words, scale or minv is written)
+ *   codes     device, words in `layout` for n tokens per (b, h), as
+ *             cq_quantize_kv writes them; only the words of rows
+ *             [t0, t0 + m) are written
+ *   scale     device, float32 [B][H][d]: (mx - mn)/L correctly rounded
+ *   minv      device, float32 [B][H][d]: mn
+ *   code(i, j) = round-half-to-even((x_ij - mn_j)*L/(mx_j - mn_j)) decided
+ *   exactly and clamped to [0, L] (a value outside the range takes the
+ *   nearest end level).  With mn/mx the range of rows [0, n) and t0 = 0,
+ *   m = n, the outputs equal cq_quantize_kv's bit for bit.
+ *   Requires t0 % 32 == 0, m % 32 == 0 unless t0 + m == n (a V word holds
+ *   whole 32-token groups), t0 + m <= n, t0 + m <= x_rows, d*b % 32 == 0,
+ *   d == 128 (else UNSUPPORTED).  m == 0 writes nothing.
+ */
+cq_status cq_quantize_kv_rows(const void* x, cq_dtype x_dtype,
+                              int32_t B, int32_t H, int32_t x_rows,
+                              int32_t t0, int32_t m, int32_t d, int32_t bits,
+                              cq_layout layout,
+                              const float* mn, const float* mx,
+                              const uint32_t* unit_mask, int32_t n,
+                              uint32_t* codes, float* scale, float* minv,
+                              void* stream);
+
+/* ------------------------------------------------------------------------
  * cq_decode_attn — one decode step of attention over a quantized visual
  * cache plus a full-precision text tail ([ART] Method parts 2 and 3; only
  * the visual cache is quantized, [ABS]).

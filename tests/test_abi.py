@@ -144,3 +144,51 @@ def test_score_entry_points_reject():
     assert f16(q=None) == 1 and f16(k=None) == 1 and f16(out=None) == 1 and f16(N=0) == 1
     assert f16(k=ODD) == 1 and f16(Hq=30) == 1
     assert f16(d=64) == 2 and f16(Hq=80) == 2
+
+
+def _range(**kw):
+    a = dict(x=FAKE, dt=cqb.CQ_F16, B=2, H=8, rows=1024, t0=0, m=512, d=128, mn=FAKE, mx=FAKE, reset=1, grew=None)
+    a.update(kw)
+    return lib.cq_kv_range_update(a["x"], a["dt"], a["B"], a["H"], a["rows"], a["t0"], a["m"], a["d"], a["mn"],
+                                  a["mx"], a["reset"], a["grew"], None)
+
+
+def _rows(**kw):
+    a = dict(x=FAKE, dt=cqb.CQ_F16, B=2, H=8, rows=1024, t0=0, m=512, d=128, bits=1, layout=cqb.CQ_LAYOUT_K,
+             mn=FAKE, mx=FAKE, mask=None, n=1024, codes=FAKE, scale=FAKE, minv=FAKE)
+    a.update(kw)
+    return lib.cq_quantize_kv_rows(a["x"], a["dt"], a["B"], a["H"], a["rows"], a["t0"], a["m"], a["d"], a["bits"],
+                                   a["layout"], a["mn"], a["mx"], a["mask"], a["n"], a["codes"], a["scale"],
+                                   a["minv"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(mn=None), 1), (dict(mx=None), 1), (dict(dt=5), 1), (dict(t0=-32), 1),
+    (dict(m=-1), 1), (dict(t0=768), 1),                # t0 + m > x_rows
+    (dict(m=0), 1),                                    # a reset needs a row
+    (dict(reset=2), 1), (dict(B=-1), 1), (dict(x=ODD), 1), (dict(grew=ctypes.c_void_p(0x10002)), 1),
+    (dict(d=64, rows=64, m=64), 2),
+])
+def test_range_update_rejects(kw, status):
+    assert _range(**kw) == status
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(x=None), 1), (dict(codes=None), 1), (dict(mn=None), 1), (dict(mx=None), 1), (dict(scale=None), 1),
+    (dict(minv=None), 1), (dict(bits=3), 1), (dict(layout=2), 1), (dict(dt=4), 1),
+    (dict(t0=16), 1),                                  # not on a 32-token boundary
+    (dict(m=100), 1),                                  # ragged, and not the segment's end
+    (dict(t0=768), 1), (dict(n=512, t0=32), 1),        # past the code buffer
+    (dict(rows=256), 1),                               # past x
+    (dict(x=ODD), 1), (dict(codes=ODD), 1), (dict(mask=ctypes.c_void_p(0x10002)), 1),
+    (dict(d=48), 1), (dict(d=64, rows=64, m=64, n=64), 2),
+])
+def test_quantize_rows_rejects(kw, status):
+    assert _rows(**kw) == status
+
+
+def test_rows_calls_without_work_are_no_ops():
+    assert _range(B=0, x=None, mn=None, mx=None) == 0
+    assert _range(m=0, reset=0, x=None) == 0                        # nothing to merge, no flag to clear
+    assert _rows(B=0, x=None, codes=None, mn=None, mx=None, scale=None, minv=None) == 0
+    assert _rows(m=0, x=None, codes=None, scale=None, minv=None) == 0
