@@ -25,7 +25,11 @@ Sweeps (not the headline line; one JSON line per point, then a table):
                            full decode step over all layers);
                            graph: one 32-layer decode step issued layer by
                            layer and replayed as one captured HIP graph
-                           (B=16 n=3328, B=64 n=8192).  No name: all three
+                           (B=16 n=3328, B=64 n=8192);
+                           stream: chunked prefill of the long-context
+                           cache (range updates per 512/2048-token chunk,
+                           final codes, eager codes) against the one-shot
+                           quantization.  No name: all four
 
 Profiling helpers (used to produce profiles/):
     --only {step,copy}     run only the timed steps, or only a 1 GiB copy
@@ -372,7 +376,7 @@ def sweeps(args):
         rows.append(row)
         print(json.dumps(row), flush=True)
 
-    which = set(args.sweeps) or {"bits", "budget", "graph"}
+    which = set(args.sweeps) or {"bits", "budget", "graph", "stream"}
     layers, Hq, Hkv, d, T = 32, 32, 8, 128, 64
     calib = (0.9, 0.0, 0.8, 0.0)
 
@@ -493,12 +497,56 @@ def sweeps(args):
             del stack, qs, outs, graphed
             torch.cuda.empty_cache()
 
+    def stream_sweep():
+        """chunked prefill of the long-context cache (B=64, 8 kv heads, n=8192):
+        per-chunk range updates and the final row codes, deferred and eager,
+        against the one-shot fused quantization"""
+        from extreme_bit_kv_amd.prefill import ChunkedVisualQuantizer
+        B, H, n = 64, 8, 8192
+        K = kv_torch(7, 0, ROLE_K, B, H, n, d, "float16", dev)
+        V = kv_torch(7, 0, ROLE_V, B, H, n, d, "float16", dev)
+        x_bytes = B * H * n * d * 2
+        code_bytes = B * H * n * d // 8
+        t = timed(lambda: (cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K), cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)),
+                  args.steps)
+        emit({"sweep": "stream", "mode": "one-shot", "chunk": n, "B": B, "n": n, "ms": round(t * 1e3, 4),
+              "seq_steps_per_s": round(B / t, 1), "GBs": round(2 * (x_bytes + code_bytes) / t / 1e9, 1),
+              "frac_8TBs": round(2 * (x_bytes + code_bytes) / t / 1e9 / HBM_PEAK_GBS, 4)})
+        for chunk in (512, 2048):
+            note(f"stream: chunk {chunk}")
+            q = ChunkedVisualQuantizer(K, V, n, bits=1)
+
+            def gather():
+                q.t = 0
+                for _ in range(n // chunk):
+                    q.append(chunk)
+            tr = timed(gather, args.steps)
+            tf = timed(q.finish, args.steps)
+            for mode, tt, nb in (("range updates", tr, 2 * x_bytes), ("final codes", tf, 2 * (x_bytes + code_bytes))):
+                emit({"sweep": "stream", "mode": mode, "chunk": chunk, "B": B, "n": n, "ms": round(tt * 1e3, 4),
+                      "seq_steps_per_s": round(B / tt, 1), "GBs": round(nb / tt / 1e9, 1),
+                      "frac_8TBs": round(nb / tt / 1e9 / HBM_PEAK_GBS, 4)})
+            qe = ChunkedVisualQuantizer(K, V, n, bits=1, eager=True)
+
+            def eager():
+                qe.t = 0
+                for _ in range(n // chunk):
+                    qe.append(chunk)
+            te = timed(eager, max(3, args.steps // 4))
+            emit({"sweep": "stream", "mode": "eager", "chunk": chunk, "B": B, "n": n, "ms": round(te * 1e3, 4),
+                  "seq_steps_per_s": round(B / te, 1), "GBs": None, "frac_8TBs": None})
+            del q, qe
+        del K, V
+        torch.cuda.empty_cache()
+
     if "bits" in which:
         bit_sweep()
     if "budget" in which:
         budget_sweep()
     if "graph" in which:
         graph_sweep()
+    if "stream" in which:
+        stream_sweep()
 
     # table
     print("\n| sweep | point | B | ms | seq-steps/s | GB/s | of 8 TB/s |", file=sys.stderr)
@@ -508,6 +556,8 @@ def sweeps(args):
             pt, ms = (f"b={r['bits']}" if r["bits"] < 16 else "fp16") + f", n={r['n']}", r["decode_ms"]
         elif r["sweep"] == "graph":
             pt, ms = f"{r['layers']} layers, n={r['n']}, {r['mode']}", r["step_ms"]
+        elif r["sweep"] == "stream":
+            pt, ms = f"{r['mode']}, chunk {r['chunk']}, n={r['n']}", r["ms"]
         else:
             pt, ms = f"{r['budget_GiB']} GiB, n={r['n']}, {r['cache']}", r["step_ms"]
         print(f"| {r['sweep']} | {pt} | {r['B']} | {ms} | {r['seq_steps_per_s']} | {r['GBs']} | {r['frac_8TBs']} |",
@@ -600,7 +650,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["step", "copy"], default=None)
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
-    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph"], default=None)
+    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream"], default=None)
     ap.add_argument("--command-note", default="")
     args = ap.parse_args()
     if args.summarize:
