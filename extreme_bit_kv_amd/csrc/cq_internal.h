@@ -82,6 +82,11 @@ int decode_generic_splits(int n, int units, int requested);
 size_t decode_generic_ws(int B, int Hq, int Hkv, int n, int T, int d, int splits);
 hipError_t decode_generic(const DecodeArgs& a);
 
+// b = 1, visual scores kept in LDS (one 16-wave workgroup per CU walking its units)
+bool decode_lds_supported(const DecodeArgs& a);
+bool decode_lds_preferred(const DecodeArgs& a);   // the automatic choice
+hipError_t decode_lds(const DecodeArgs& a);
+
 size_t decode_fast_ws(int B, int Hq, int Hkv, int n, int T, int d);
 bool decode_fast_supported(const DecodeArgs& a);
 hipError_t decode_fast(const DecodeArgs& a);

@@ -69,9 +69,10 @@ __host__ __device__ inline Ws carve(void* base, int units, int S) {
   return w;
 }
 
-__global__ void qf_init(Ws w, long words) {       // slot and fin are contiguous
+// slot and fin are contiguous, 16-byte aligned, a multiple of 128 words
+__global__ void qf_init(Ws w, long quads) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < words) w.slot[i] = kEmpty;
+  if (i < quads) reinterpret_cast<uint4*>(w.slot)[i] = make_uint4(kEmpty, kEmpty, kEmpty, kEmpty);
   if (i == 0) w.status[0] = 0;
 }
 
@@ -283,8 +284,8 @@ hipError_t quant_fused(const QuantArgs& a) {
   long grid = (capacity / S) * S;
   const long items = (long)units * S;
   if (grid > items) grid = items;
-  const long words = (long)units * (S + 1) * 128;
-  CQ_LAUNCH(qf_init, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, a.stream, w, words);
+  const long quads = (long)units * (S + 1) * 128 / 4;
+  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream, w, quads);
   const __half* x = (const __half*)a.x;
   int n = a.n, Sv = S, un = units;
   void* args[] = {(void*)&x, (void*)&n, (void*)&un, (void*)&Sv, (void*)&a.codes, (void*)&a.scale,

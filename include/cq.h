@@ -86,15 +86,23 @@ typedef struct {
 } cq_calib;
 
 /* Execution path selection, for tests and tuning (NULL opts = automatic).
- * CQ_PATH_FAST picks one of the matrix-core decode schedules itself (the
- * split one at b = 1 below 64 (batch, kv head) units, else the one-launch
- * one); the two FAST_ values force one (decode only; for quantization they
- * mean CQ_PATH_FAST):
+ * CQ_PATH_FAST picks one of the matrix-core decode schedules itself: at b = 1
+ * the LDS-score one when it takes the shape and every (batch, kv head) unit
+ * gets a workgroup (a CU) of its own (at most 256 units on a 256-CU MI355X),
+ * else the split one below 64 units, else the one-launch one.  The FAST_
+ * values force one (decode only; for quantization they mean CQ_PATH_FAST):
  *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head);
  *   CQ_PATH_FAST_SPLIT  b = 1 only: a key-pass launch and a value-pass launch,
- *                       each over token chunks of every (batch, kv head). */
+ *                       each over token chunks of every (batch, kv head);
+ *   CQ_PATH_FAST_LDS    b = 1 only, G * ceil(n/128) <= 256 (n <= 8192 at
+ *                       G = 4): one launch, one workgroup per CU walking its
+ *                       (batch, kv head) units, the visual scores kept in LDS
+ *                       between the key and the value pass (the keys are
+ *                       read once); results equal CQ_PATH_FAST_ONE's bit for
+ *                       bit. */
 typedef enum {
-  CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4
+  CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4,
+  CQ_PATH_FAST_LDS = 5
 } cq_path;
 typedef struct {
   int32_t path;     /* cq_path; a FAST path on an unsupported shape -> CQ_ERR_UNSUPPORTED */

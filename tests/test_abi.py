@@ -85,7 +85,10 @@ def _decode(**kw):
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
-    (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0))), 1),              # no such path
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0))), 1),              # no such path
+    (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), bits=2), 2),     # LDS-score schedule: b = 1 only ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), n=8320), 2),     # ... and G x ceil(n/128) <= 256
+    (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), Hq=24), 2),      # ... and G in 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),      # one-launch schedule: group sizes 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), bits=2), 2),     # split schedule: b = 1 only
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=0, kc=None, vc=None), 2),   # ... and n > 0
