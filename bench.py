@@ -3,8 +3,8 @@
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload long_n8192]
 
 One step is one pass of the whole path over one batch of the workload: the
-prefill quantization of the full visual K and V caches (cq_quantize_kv, twice)
-followed by one calibrated decode-attention step for every sequence
+prefill quantization of the full visual K and V caches (one cq_quantize_kv_pair
+call: both tensors in one launch) followed by one calibrated decode-attention step for every sequence
 (cq_decode_attn).  Inputs are seeded synthetic tensors already resident in HBM
 when timing starts.  W untimed steps run first, then exactly K steps are timed
 with the device synchronized on both sides; HIP events on the launch stream
@@ -214,51 +214,44 @@ def run(args):
     calib = cfg.calib
 
     # preallocated outputs and workspaces: the timed loop allocates nothing
-    kc, ks, km = cqb.cq_quantize_kv(K, cfg.bits, cqb.CQ_LAYOUT_K)
-    vc, vs, vm = cqb.cq_quantize_kv(V, cfg.bits, cqb.CQ_LAYOUT_V)
-    qws = torch.empty(max(1, cqb.lib.cq_quantize_kv_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
+    (kc, ks, km), (vc, vs, vm) = cqb.cq_quantize_kv_pair(K, V, cfg.bits)
+    qws = torch.empty(max(1, cqb.lib.cq_quantize_kv_pair_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
                       dtype=torch.uint8, device=dev)
     dws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d,
                                                               cfg.bits)), dtype=torch.uint8, device=dev)
     out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float16, device=dev)
 
-    def quant_k():
-        cqb.cq_quantize_kv(K, cfg.bits, cqb.CQ_LAYOUT_K, codes=kc, scale=ks, minv=km, workspace=qws)
-
-    def quant_v():
-        cqb.cq_quantize_kv(V, cfg.bits, cqb.CQ_LAYOUT_V, codes=vc, scale=vs, minv=vm, workspace=qws)
+    def quant():
+        cqb.cq_quantize_kv_pair(K, V, cfg.bits, k_out=(kc, ks, km), v_out=(vc, vs, vm), workspace=qws)
 
     def decode():
         cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=cfg.bits, sm_scale=sm,
                            calib=calib, out=out, workspace=dws)
 
     for _ in range(args.warmup):
-        quant_k(); quant_v(); decode()
+        quant()
+        decode()
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
         ev[k][0].record(stream)
-        quant_k()
+        quant()
         ev[k][1].record(stream)
-        quant_v()
-        ev[k][2].record(stream)
         decode()
-        ev[k][3].record(stream)
+        ev[k][2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    tq_k = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    tq_v = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
-    td = np.mean([e[2].elapsed_time(e[3]) for e in ev]) * 1e-3
+    tq = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
+    td = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
     print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
     if args.only == "step":
         print(json.dumps({"workload": cfg.name, "steps": args.steps, "ms_per_step": wall * 1e3 / args.steps,
-                          "per_call_ms": {"quantize_k": tq_k * 1e3, "quantize_v": tq_v * 1e3,
-                                          "decode_in_step": td * 1e3}}), flush=True)
+                          "per_call_ms": {"quantize_kv_pair": tq * 1e3, "decode_in_step": td * 1e3}}), flush=True)
         return
 
     # decode alone with the Infinity Cache flushed before every call
@@ -292,8 +285,7 @@ def run(args):
     tf16 = np.median([a.elapsed_time(b) for a, b in fcold]) * 1e-3
     del Kf, Vf
 
-    qb, db, fb = quant_bytes(cfg), decode_bytes(cfg), fp16_bytes(cfg)
-    tq = 0.5 * (tq_k + tq_v)
+    qb, db, fb = 2 * quant_bytes(cfg), decode_bytes(cfg), fp16_bytes(cfg)     # qb: K and V in one launch
 
     def roof(nbytes, secs, op):
         ach = nbytes / secs / 1e9
@@ -301,7 +293,7 @@ def run(args):
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
 
-    dominant = "quantize" if 2 * tq >= td else "decode"
+    dominant = "quantize" if tq >= td else "decode"
     line = {
         "metric": METRIC,
         "value": round(cfg.B * args.steps / wall, 1),
@@ -317,11 +309,12 @@ def run(args):
         "data": "synthetic (seeded outlier-channel K/V, N(0,1) q)",
         "config": {"workload": cfg.name, "B": cfg.B, "Hq": cfg.Hq, "Hkv": cfg.Hkv, "n": cfg.n, "T": cfg.T,
                    "d": cfg.d, "bits": cfg.bits, "calib": list(calib) if calib else None,
-                   "step": "quantize K + quantize V (full prefill cache) + 1 decode step"},
+                   "step": "quantize K and V of the full prefill cache (one cq_quantize_kv_pair call) "
+                           "+ 1 decode step"},
         "roofline": roof(qb if dominant == "quantize" else db, tq if dominant == "quantize" else td, dominant),
-        "dominant_kernel": "cq_quantize_kv" if dominant == "quantize" else "cq_decode_attn",
-        "per_call_ms": {"quantize_k": round(tq_k * 1e3, 4), "quantize_v": round(tq_v * 1e3, 4),
-                        "decode_in_step": round(td * 1e3, 4), "decode_cold": round(td_cold * 1e3, 4)},
+        "dominant_kernel": "cq_quantize_kv_pair" if dominant == "quantize" else "cq_decode_attn",
+        "per_call_ms": {"quantize_kv_pair": round(tq * 1e3, 4), "decode_in_step": round(td * 1e3, 4),
+                        "decode_cold": round(td_cold * 1e3, 4)},
         "decode": {"seq_steps_per_s_cold": round(cfg.B / td_cold, 1),
                    "roofline_cold": roof(db, td_cold, "decode"),
                    "roofline_in_step": roof(db, td, "decode")},

@@ -34,7 +34,7 @@ CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLI
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
             "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16", "cq_kv_range_update",
-            "cq_quantize_kv_rows")
+            "cq_quantize_kv_rows", "cq_quantize_kv_pair_workspace", "cq_quantize_kv_pair")
 
 
 class cq_calib(ctypes.Structure):
@@ -59,6 +59,10 @@ lib.cq_quantize_kv_workspace.argtypes = [_i32] * 5
 lib.cq_quantize_kv.restype = _i32
 lib.cq_quantize_kv.argtypes = [_vp, _i32, _i32, _i32, _i32, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz,
                                ctypes.POINTER(cq_opts), _vp]
+lib.cq_quantize_kv_pair_workspace.restype = _sz
+lib.cq_quantize_kv_pair_workspace.argtypes = [_i32] * 5
+lib.cq_quantize_kv_pair.restype = _i32
+lib.cq_quantize_kv_pair.argtypes = [_vp, _vp, _i32] + [_i32] * 5 + [_vp] * 6 + [_vp, _sz, ctypes.POINTER(cq_opts), _vp]
 lib.cq_kv_range_update.restype = _i32
 lib.cq_kv_range_update.argtypes = [_vp, _i32] + [_i32] * 6 + [_vp, _vp, _i32, _vp, _vp]
 lib.cq_quantize_kv_rows.restype = _i32
@@ -279,6 +283,39 @@ def cq_decode_attn_fp16(q, k, v, sm_scale: float, out=None, workspace=None):
                                  _stream(q.device))
     _check(st, "cq_decode_attn_fp16")
     return out
+
+
+def cq_quantize_kv_pair(k, v, bits: int, k_out=None, v_out=None, workspace=None, path: int = CQ_PATH_AUTO):
+    """One layer's K and V [B, H, n, d] (same shape and dtype) quantized in one
+    call.  Returns ((k_codes, k_scale, k_min), (v_codes, v_scale, v_min)) in
+    the K and V layouts; k_out / v_out may pass those buffers."""
+    torch = _torch()
+    _need(k, "k")
+    _need(v, "v", tuple(k.shape), k.dtype, k.device)
+    B, H, n, d = k.shape
+    dev = k.device
+
+    def outs(given, layout, name):
+        if given is None:
+            given = (torch.empty(code_words_shape(B, H, n, d, bits, layout), dtype=torch.int32, device=dev),
+                     torch.empty((B, H, d), dtype=torch.float32, device=dev),
+                     torch.empty((B, H, d), dtype=torch.float32, device=dev))
+        codes, scale, minv = given
+        _need(codes, f"{name}_codes", code_words_shape(B, H, n, d, bits, layout), torch.int32, dev)
+        _need(scale, f"{name}_scale", (B, H, d), torch.float32, dev)
+        _need(minv, f"{name}_min", (B, H, d), torch.float32, dev)
+        return given
+    kc, ks, km = outs(k_out, CQ_LAYOUT_K, "k")
+    vc, vs, vm = outs(v_out, CQ_LAYOUT_V, "v")
+    ws_bytes = lib.cq_quantize_kv_pair_workspace(B, H, n, d, bits)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    opts = cq_opts(path, 0)
+    st = lib.cq_quantize_kv_pair(_ptr(k), _ptr(v), _dtype_code(k), B, H, n, d, bits, _ptr(kc), _ptr(ks), _ptr(km),
+                                 _ptr(vc), _ptr(vs), _ptr(vm), _ptr(workspace),
+                                 0 if workspace is None else workspace.numel(), ctypes.byref(opts), _stream(dev))
+    _check(st, "cq_quantize_kv_pair")
+    return (kc, ks, km), (vc, vs, vm)
 
 
 def _rows_ptr(x, row0: int, t0: int, m: int):

@@ -6,7 +6,7 @@ packed codes plus the full-precision text tokens (CalibQuant abstract; QbitAI
 article, "Method").  This module is that integration point, and nothing more:
 
 * ``QuantizedVisualKV`` quantizes one layer's visual K and V at prefill
-  (``cq_quantize_kv``, channel-wise b-bit, packed codes + scale + minimum);
+  (``cq_quantize_kv_pair``, channel-wise b-bit, packed codes + scale + minimum);
 * ``CalibQuantAttention`` is the per-layer decode attention
   (``cq_decode_attn``: post-scaled scores, calibration g, softmax over visual
   and text tokens, post-scaled values), with its workspace kept across calls;
@@ -23,7 +23,7 @@ from typing import List, Optional, Sequence
 
 import torch
 
-from ._binding import CQ_LAYOUT_K, CQ_LAYOUT_V, cq_decode_attn, cq_quantize_kv, lib
+from ._binding import cq_decode_attn, cq_quantize_kv_pair, lib
 
 
 class QuantizedVisualKV:
@@ -40,8 +40,7 @@ class QuantizedVisualKV:
         if k_visual.shape != v_visual.shape:
             raise ValueError(f"K {tuple(k_visual.shape)} and V {tuple(v_visual.shape)} differ")
         self.B, self.Hkv, self.n, self.d = k_visual.shape
-        self.k = cq_quantize_kv(k_visual, bits, CQ_LAYOUT_K)      # (codes, scale, min)
-        self.v = cq_quantize_kv(v_visual, bits, CQ_LAYOUT_V)
+        self.k, self.v = cq_quantize_kv_pair(k_visual, v_visual, bits)   # each (codes, scale, min)
 
     @classmethod
     def from_codes(cls, k, v, n: int, bits: int) -> "QuantizedVisualKV":

@@ -94,6 +94,54 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
 }
 
 // ---------------------------------------------------------------------------
+size_t cq_quantize_kv_pair_workspace(int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits) {
+  if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits)) return 0;
+  const size_t one = cq_quantize_kv_workspace(B, H, n, d, bits);
+  const size_t pair = cqi::quant_fused_pair_ws(B, H, n, d);
+  return one > pair ? one : pair;
+}
+
+cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, int32_t B, int32_t H, int32_t n,
+                              int32_t d, int32_t bits, uint32_t* k_codes, float* k_scale, float* k_min,
+                              uint32_t* v_codes, float* v_scale, float* v_min, void* workspace,
+                              size_t workspace_bytes, const cq_opts* opts, void* stream) {
+  if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype)) return CQ_ERR_INVALID_ARG;
+  if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
+  const int path = opt_path(opts);
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS) return CQ_ERR_INVALID_ARG;
+  const int64_t units = (int64_t)B * H;
+  if (units > 0) {
+    if (k_scale == nullptr || k_min == nullptr || v_scale == nullptr || v_min == nullptr) return CQ_ERR_INVALID_ARG;
+    if (n > 0 && (k == nullptr || v == nullptr || k_codes == nullptr || v_codes == nullptr)) return CQ_ERR_INVALID_ARG;
+    if (!al16(k) || !al16(v) || !al16(k_codes) || !al16(v_codes) || !al4(k_scale) || !al4(k_min) ||
+        !al4(v_scale) || !al4(v_min) || !al16(workspace))
+      return CQ_ERR_INVALID_ARG;
+  }
+  if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
+  cqi::QuantArgs ka{k, x_dtype, B, H, n, d, bits, CQ_LAYOUT_K, k_codes, k_scale, k_min, workspace,
+                    (hipStream_t)stream};
+  cqi::QuantArgs va{v, x_dtype, B, H, n, d, bits, CQ_LAYOUT_V, v_codes, v_scale, v_min, workspace,
+                    (hipStream_t)stream};
+  const bool pair_ok = cqi::quant_fused_pair_supported(ka) && path != CQ_PATH_GENERIC;
+  if (pair_ok) {
+    const size_t need = cqi::quant_fused_pair_ws(B, H, n, d);
+    if (workspace == nullptr || workspace_bytes < need) return CQ_ERR_WORKSPACE;
+    clear_stale_hip_error();
+    return from_hip(cqi::quant_fused_pair(ka, va));
+  }
+  // one tensor after the other, sharing the workspace (stream order keeps them apart)
+  const bool fused_ok = cqi::quant_fused_supported(ka) && cqi::quant_fused_supported(va);
+  if (path >= CQ_PATH_FAST && !fused_ok) return CQ_ERR_UNSUPPORTED;
+  const bool use_fused = fused_ok && path != CQ_PATH_GENERIC;
+  const size_t need = use_fused ? cqi::quant_fused_ws(B, H, n, d) : cqi::quant_generic_ws(B, H, n, d);
+  if (need > 0 && units > 0 && n > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
+  clear_stale_hip_error();
+  const hipError_t e = use_fused ? cqi::quant_fused(ka) : cqi::quant_generic(ka);
+  if (e != hipSuccess) return from_hip(e);
+  return from_hip(use_fused ? cqi::quant_fused(va) : cqi::quant_generic(va));
+}
+
+// ---------------------------------------------------------------------------
 cq_status cq_kv_range_update(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, int32_t x_rows, int32_t t0,
                              int32_t m, int32_t d, float* mn, float* mx, int32_t reset, uint32_t* grew,
                              void* stream) {

@@ -39,6 +39,10 @@ hipError_t quant_generic(const QuantArgs& a);
 size_t quant_fused_ws(int B, int H, int n, int d);
 bool quant_fused_supported(const QuantArgs& a);
 hipError_t quant_fused(const QuantArgs& a);
+// K (CQ_LAYOUT_K) and V (CQ_LAYOUT_V) of one layer in one launch; k.ws holds both tensors' words
+size_t quant_fused_pair_ws(int B, int H, int n, int d);
+bool quant_fused_pair_supported(const QuantArgs& a);
+hipError_t quant_fused_pair(const QuantArgs& k, const QuantArgs& v);
 
 // ---- chunked prefill: range update and row quantization ----------------
 struct RowsArgs {

@@ -246,9 +246,37 @@ __global__ void __launch_bounds__(kWaves * 64) qf_b1(const __half* __restrict__ 
   }
 }
 
+// K and V of one layer in one launch: the items of K (each (unit, chunk))
+// come first, then those of V, each tensor with rendezvous words of its own.
+// The boundary between them is a multiple of the chunk count, so all chunks
+// of a unit still run in the same round.  One launch saves the second word
+// reset, launch gap and first and last round of two separate calls.
+__global__ void __launch_bounds__(kWaves * 64) qf_b1_pair(const __half* __restrict__ xk, const __half* __restrict__ xv,
+                                                          int n, int units, int S, uint32_t* __restrict__ kcodes,
+                                                          float* __restrict__ kscale, float* __restrict__ kminv,
+                                                          uint32_t* __restrict__ vcodes, float* __restrict__ vscale,
+                                                          float* __restrict__ vminv, Ws wk, Ws wv) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int pair = 4 * wave + (lane >> 4), k = lane & 15;
+  __shared__ Smem sm;
+  const long per = (long)units * S;
+  uint4 v[kRows];
+  // the same item order as one loop over both tensors, as two loops (each
+  // with the register use of its own layout)
+  long item = blockIdx.x;
+  for (; item < per; item += gridDim.x) {
+    load_chunk(v, xk, n, item, S, pair, k);
+    qf_item<CQ_LAYOUT_K>(v, item, n, S, kcodes, kscale, kminv, wk, sm);
+  }
+  for (; item < 2 * per; item += gridDim.x) {
+    load_chunk(v, xv, n, item - per, S, pair, k);
+    qf_item<CQ_LAYOUT_V>(v, item - per, n, S, vcodes, vscale, vminv, wv, sm);
+  }
+}
+
 // Co-resident workgroups of `fn` on the current device (cached per device and layout).
 long capacity_of(const void* fn, int layout) {
-  static long cache[64][2];
+  static long cache[64][3];
   int dev = 0, cus = 0, per_cu = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
   if (cache[dev][layout] > 0) return cache[dev][layout];
@@ -272,6 +300,43 @@ bool quant_fused_supported(const QuantArgs& a) {
     return false;
   const void* fn = a.layout == CQ_LAYOUT_K ? (const void*)qf_b1<CQ_LAYOUT_K> : (const void*)qf_b1<CQ_LAYOUT_V>;
   return capacity_of(fn, a.layout == CQ_LAYOUT_K ? 0 : 1) >= (a.n + kChunk - 1) / kChunk;
+}
+
+// K and V together: the two tensors' words follow each other in the workspace
+// (one status word), reset by one launch.
+size_t quant_fused_pair_ws(int B, int H, int n, int d) {
+  const int S = (n + kChunk - 1) / kChunk;
+  return ws_bytes(B * H, S) + (ws_bytes(B * H, S) - 256);
+}
+
+bool quant_fused_pair_supported(const QuantArgs& a) {
+  if (!(a.dtype == CQ_F16 && a.bits == 1 && a.d == 128 && a.n >= 1 && a.n <= (1 << 20) && (long)a.B * a.H >= 1))
+    return false;
+  return capacity_of((const void*)qf_b1_pair, 2) >= (a.n + kChunk - 1) / kChunk;
+}
+
+hipError_t quant_fused_pair(const QuantArgs& k, const QuantArgs& v) {
+  const int units = k.B * k.H;
+  const int S = (k.n + kChunk - 1) / kChunk;
+  Ws wk = carve(k.ws, units, S);
+  Ws wv;
+  wv.status = wk.status;
+  wv.slot = wk.fin + (size_t)units * 128;
+  wv.fin = wv.slot + (size_t)units * S * 128;
+  const void* fn = (const void*)qf_b1_pair;
+  const long capacity = capacity_of(fn, 2);
+  if (capacity < S) return hipErrorInvalidConfiguration;
+  long grid = (capacity / S) * S;
+  const long items = 2L * units * S;
+  if (grid > items) grid = items;
+  const long quads = 2L * units * (S + 1) * 128 / 4;     // both tensors' words
+  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, k.stream, wk, quads);
+  const __half* xk = (const __half*)k.x;
+  const __half* xv = (const __half*)v.x;
+  int n = k.n, Sv = S, un = units;
+  void* args[] = {(void*)&xk, (void*)&xv, (void*)&n, (void*)&un, (void*)&Sv, (void*)&k.codes, (void*)&k.scale,
+                  (void*)&k.minv, (void*)&v.codes, (void*)&v.scale, (void*)&v.minv, (void*)&wk, (void*)&wv};
+  return hipLaunchKernel(fn, dim3((unsigned)grid), dim3(kWaves * 64), args, 0, k.stream);
 }
 
 hipError_t quant_fused(const QuantArgs& a) {

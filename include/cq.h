@@ -164,6 +164,32 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype,
                          const cq_opts* opts, void* stream);
 
 /* ------------------------------------------------------------------------
+ * cq_quantize_kv_pair — one layer's visual K and V in one call: the same
+ * outputs as cq_quantize_kv(k, .., CQ_LAYOUT_K, k_codes, k_scale, k_min) and
+ * cq_quantize_kv(v, .., CQ_LAYOUT_V, v_codes, v_scale, v_min), bit for bit
+ * ([ART] Method part 1 applied to K and to V alike).
+ *
+ *   k, v      device, [B][H][n][d] of x_dtype each
+ *   k_*, v_*  as the outputs of cq_quantize_kv for CQ_LAYOUT_K / CQ_LAYOUT_V
+ *   workspace device, >= cq_quantize_kv_pair_workspace(...) bytes; its first
+ *             int32 is the status word of cq_quantize_kv
+ *   opts      NULL / CQ_PATH_AUTO: at b = 1 with float16 input the fused
+ *             kernel takes the chunks of both tensors in one launch (one
+ *             word reset, one launch); other shapes run the two tensors one
+ *             after the other.  CQ_PATH_GENERIC and CQ_PATH_FAST as for
+ *             cq_quantize_kv.
+ * Errors and limits as for cq_quantize_kv.
+ * ------------------------------------------------------------------------ */
+size_t cq_quantize_kv_pair_workspace(int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits);
+
+cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype,
+                              int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits,
+                              uint32_t* k_codes, float* k_scale, float* k_min,
+                              uint32_t* v_codes, float* v_scale, float* v_min,
+                              void* workspace, size_t workspace_bytes,
+                              const cq_opts* opts, void* stream);
+
+/* ------------------------------------------------------------------------
  * Chunked prefill: quantization of a visual segment that is written chunk by
  * chunk (a chunked prefill, or video frames appended to the segment).
  * [ART] Method part 1 takes the range per channel over the tokens of one

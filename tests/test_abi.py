@@ -195,3 +195,26 @@ def test_rows_calls_without_work_are_no_ops():
     assert _range(m=0, reset=0, x=None) == 0                        # nothing to merge, no flag to clear
     assert _rows(B=0, x=None, codes=None, mn=None, mx=None, scale=None, minv=None) == 0
     assert _rows(m=0, x=None, codes=None, scale=None, minv=None) == 0
+
+
+def _pair(**kw):
+    a = dict(k=FAKE, v=FAKE, dt=cqb.CQ_F16, B=1, H=1, n=64, d=128, bits=1, kc=FAKE, ks=FAKE, km=FAKE, vc=FAKE,
+             vs=FAKE, vm=FAKE, ws=FAKE, wsb=1 << 30, opts=None)
+    a.update(kw)
+    return lib.cq_quantize_kv_pair(a["k"], a["v"], a["dt"], a["B"], a["H"], a["n"], a["d"], a["bits"], a["kc"],
+                                   a["ks"], a["km"], a["vc"], a["vs"], a["vm"], a["ws"], a["wsb"], a["opts"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), 1), (dict(v=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(ks=None), 1),
+    (dict(vm=None), 1), (dict(bits=3), 1), (dict(dt=7), 1), (dict(n=-1), 1), (dict(d=48), 1), (dict(d=64), 2),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(9, 0))), 1), (dict(v=ODD), 1), (dict(vc=ODD), 1), (dict(ws=ODD), 1),
+])
+def test_quantize_pair_rejects(kw, status):
+    assert _pair(**kw) == status
+
+
+def test_quantize_pair_workspace_query():
+    assert lib.cq_quantize_kv_pair_workspace(64, 8, 8192, 128, 1) >= lib.cq_quantize_kv_workspace(64, 8, 8192, 128, 1)
+    assert lib.cq_quantize_kv_pair_workspace(1, 1, 256, 128, 3) == 0
+    assert _pair(B=0, k=None, v=None, kc=None, ks=None, km=None, vc=None, vs=None, vm=None, ws=None, wsb=0) == 0
