@@ -119,7 +119,7 @@ def source_digest(*names):
 
 
 KERNEL_SOURCES = {
-    "quantize": ("quantize_fused.hip", "quantize_generic.hip", "cq_device.h"),
+    "quantize": ("quantize_fused.hip", "quantize_generic.hip", "cq_device.h", "cq_tile1.h"),
     "decode": ("decode_fast.hip", "decode_split.hip", "decode_generic.hip", "cq_device.h", "cq_mfma.h"),
 }
 

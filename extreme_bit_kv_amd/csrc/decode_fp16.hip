@@ -83,14 +83,15 @@ __global__ void __launch_bounds__(kThreads) f16_split(Shape sh, const __half* __
     for (int c = 0; c < 8; ++c) acc[g][c] = 0.f;
   }
   for (int base = t0 + wave * 4 * kRows; base < t1; base += kStep) {
-    // rows past the split re-read its last row (in bounds) and get p = 0
+    // rows past the split re-read its last row (in bounds) and get p = 0;
+    // K and V are read once, so the loads are non-temporal
     uint4 kr[kRows], vr[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
-      kr[r] = *reinterpret_cast<const uint4*>(ku + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
+      kr[r] = cqd::ld_nt(ku + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
-      vr[r] = *reinterpret_cast<const uint4*>(vu + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
+      vr[r] = cqd::ld_nt(vu + (size_t)min(base + r * 4 + sub, t1 - 1) * kD);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s[kRows];

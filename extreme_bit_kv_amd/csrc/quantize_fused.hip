@@ -90,7 +90,9 @@ struct Smem {
 };
 
 // Register tile of one item: channels 8k..8k+7 of tokens base + 16 pair + it
-// (rows past n repeat the last row).
+// (rows past n repeat the last row).  The input is read once, so the loads
+// are non-temporal, which shortens each workgroup's load phase (a round's
+// time is a chain of latencies: load, rendezvous, codes).
 __device__ __forceinline__ void load_chunk(uint4 (&v)[kRows], const __half* __restrict__ x, int n, long item,
                                            int S, int pair, int k) {
   const int u = (int)(item / S), s = (int)(item % S);
@@ -99,7 +101,7 @@ __device__ __forceinline__ void load_chunk(uint4 (&v)[kRows], const __half* __re
 #pragma unroll
   for (int it = 0; it < kRows; ++it) {
     const int tok = min(base + kRows * pair + it, n - 1);
-    v[it] = *reinterpret_cast<const uint4*>(xu + (size_t)tok * 128 + 8 * k);
+    v[it] = cqd::ld_nt(xu + (size_t)tok * 128 + 8 * k);
   }
 }
 

@@ -171,7 +171,7 @@ __global__ void __launch_bounds__(kWaves * 64) qr_b1(const __half* __restrict__ 
 #pragma unroll
   for (int it = 0; it < kRows; ++it) {
     const int tok = min(base + kRows * pair + it, last);
-    v[it] = *reinterpret_cast<const uint4*>(xu + (size_t)tok * 128 + 8 * k);
+    v[it] = cqd::ld_nt(xu + (size_t)tok * 128 + 8 * k);   // the rows' last read
   }
   __shared__ uint32_t thr[64];                 // per channel pair: float16 thresholds
   if (tid < 128) {
