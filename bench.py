@@ -234,20 +234,23 @@ def run(args):
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # events at step boundaries and between the two calls: a step's decode
+    # ends at the event where the next step's quantize starts, so every step
+    # carries two events (each costs a few microseconds of queue time)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    ev[0].record(stream)
     for k in range(args.steps):
-        ev[k][0].record(stream)
         quant()
-        ev[k][1].record(stream)
+        ev[2 * k + 1].record(stream)
         decode()
-        ev[k][2].record(stream)
+        ev[2 * k + 2].record(stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
-    tq = np.mean([e[0].elapsed_time(e[1]) for e in ev]) * 1e-3
-    td = np.mean([e[1].elapsed_time(e[2]) for e in ev]) * 1e-3
+    tq = np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]) * 1e-3
+    td = np.mean([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]) * 1e-3
     print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
     if args.only == "step":
         print(json.dumps({"workload": cfg.name, "steps": args.steps, "ms_per_step": wall * 1e3 / args.steps,
