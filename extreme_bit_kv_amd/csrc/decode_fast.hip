@@ -154,7 +154,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   };
   // The first kPreTail tail keys, as (token 4 wave + lane/16 + 32 r, channels
   // 8 (lane%16) ..+7), are requested first: their scores are formed right
-  // after the prologue, while the first key tiles are still in flight.
+  // after the prologue, while the first key tiles are still in flight.  The
+  // tail is read once and, unlike the codes, is not in the cache from a
+  // producer just before, so its loads are non-temporal.
   const int tsub = lane >> 4, tcl = lane & 15;
   constexpr int kKtRounds = kPreTail / (4 * kWaves);
   uint4 ktp[kKtRounds][2];
@@ -164,10 +166,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     const size_t e = ((size_t)unit * T + max(min(j, T - 1), 0)) * 128 + 8 * tcl;
     if constexpr (F32) {
       const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
-      ktp[r][0] = src[0];
-      ktp[r][1] = src[1];
+      ktp[r][0] = cqd::ld_nt(src);
+      ktp[r][1] = cqd::ld_nt(src + 1);
     } else {
-      ktp[r][0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const __half*>(ktb) + e);
+      ktp[r][0] = cqd::ld_nt(reinterpret_cast<const __half*>(ktb) + e);
       ktp[r][1] = make_uint4(0, 0, 0, 0);
     }
   }
@@ -375,7 +377,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       vtr[i][0] = x.x;
       vtr[i][F32 ? 1 : 0] = x.y;
     } else {
-      vtr[i][0] = *reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e);
+      vtr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
