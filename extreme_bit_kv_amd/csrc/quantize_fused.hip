@@ -107,10 +107,14 @@ __device__ __forceinline__ void load_chunk(uint4 (&v)[kRows], const __half* __re
 
 // One item: range of the chunk in `v`, the unit's rendezvous, codes and
 // stores.
+constexpr int kPfRows = kRows / 2;    // rows of the next item requested into LDS during a rendezvous
+typedef uint4 PfBuf[kPfRows][kWaves][64];
+
 template <int LAYOUT>
 __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int n, int S,
                                         uint32_t* __restrict__ codes, float* __restrict__ scale,
-                                        float* __restrict__ minv, const Ws& w, Smem& sm) {
+                                        float* __restrict__ minv, const Ws& w, Smem& sm,
+                                        const __half* nx = nullptr, int nbase = 0, PfBuf* pf = nullptr) {
   constexpr int IT = kRows;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane >> 4, k = lane & 15;
@@ -154,6 +158,17 @@ __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int 
       const uint32_t word = (uint32_t)__half_as_ushort(__float2half_rn(lo_v)) |
                             ((uint32_t)__half_as_ushort(__float2half_rn(hi_v)) << 16);
       st_word(w.slot + ((size_t)u * S + s) * 128 + tid, word);
+    }
+    if (pf != nullptr && nx != nullptr && !leader) {
+      // the first rows of this thread's part of the next item go straight to
+      // LDS while the rendezvous waits (each wave its own slots; the barrier
+      // before the thresholds are read waits for them)
+#pragma unroll
+      for (int it = 0; it < kPfRows; ++it) {
+        const int tok = min(nbase + kRows * pair + it, n - 1);
+        __builtin_amdgcn_global_load_lds(reinterpret_cast<const uint4*>(nx + (size_t)tok * 128 + 8 * k),
+                                         &(*pf)[it][wave][0], 16, 0, 0);
+      }
     }
     uint32_t uw = 0;
     if (leader) {
@@ -253,6 +268,11 @@ __global__ void __launch_bounds__(kWaves * 64) qf_b1(const __half* __restrict__ 
 // The boundary between them is a multiple of the chunk count, so all chunks
 // of a unit still run in the same round.  One launch saves the second word
 // reset, launch gap and first and last round of two separate calls.
+// A workgroup that is not its unit's leader requests the first half of its
+// next item straight into LDS as soon as it has published its chunk range:
+// the rendezvous wait covers those loads, and the next item streams only the
+// other half.  The leader does not: its gather is on every chunk's critical
+// path, and a poll returns only after the loads issued before it.
 __global__ void __launch_bounds__(kWaves * 64) qf_b1_pair(const __half* __restrict__ xk, const __half* __restrict__ xv,
                                                           int n, int units, int S, uint32_t* __restrict__ kcodes,
                                                           float* __restrict__ kscale, float* __restrict__ kminv,
@@ -261,18 +281,43 @@ __global__ void __launch_bounds__(kWaves * 64) qf_b1_pair(const __half* __restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int pair = 4 * wave + (lane >> 4), k = lane & 15;
   __shared__ Smem sm;
-  const long per = (long)units * S;
+  __shared__ __align__(16) PfBuf pf;
+  const long per = (long)units * S, total = 2 * per;
   uint4 v[kRows];
-  // the same item order as one loop over both tensors, as two loops (each
-  // with the register use of its own layout)
+  bool have = false;
+  auto next_src = [&](long nitem, int& nbase) -> const __half* {
+    if (nitem >= total) return nullptr;
+    const long nl = nitem < per ? nitem : nitem - per;
+    nbase = (int)(nl % S) * kChunk;
+    return (nitem < per ? xk : xv) + (size_t)(nl / S) * n * 128;
+  };
+  auto fetch = [&](const __half* x, long li) {
+    if (!have) {
+      load_chunk(v, x, n, li, S, pair, k);
+      return;
+    }
+    const int base = (int)(li % S) * kChunk;
+    const __half* xu = x + (size_t)(li / S) * n * 128;
+#pragma unroll
+    for (int it = 0; it < kPfRows; ++it) v[it] = pf[it][wave][lane];
+#pragma unroll
+    for (int it = kPfRows; it < kRows; ++it)
+      v[it] = cqd::ld_nt(xu + (size_t)min(base + kRows * pair + it, n - 1) * 128 + 8 * k);
+  };
   long item = blockIdx.x;
   for (; item < per; item += gridDim.x) {
-    load_chunk(v, xk, n, item, S, pair, k);
-    qf_item<CQ_LAYOUT_K>(v, item, n, S, kcodes, kscale, kminv, wk, sm);
+    fetch(xk, item);
+    int nbase = 0;
+    const __half* nx = next_src(item + gridDim.x, nbase);
+    qf_item<CQ_LAYOUT_K>(v, item, n, S, kcodes, kscale, kminv, wk, sm, nx, nbase, &pf);
+    have = nx != nullptr && item % S != 0;
   }
-  for (; item < 2 * per; item += gridDim.x) {
-    load_chunk(v, xv, n, item - per, S, pair, k);
-    qf_item<CQ_LAYOUT_V>(v, item - per, n, S, vcodes, vscale, vminv, wv, sm);
+  for (; item < total; item += gridDim.x) {
+    fetch(xv, item - per);
+    int nbase = 0;
+    const __half* nx = next_src(item + gridDim.x, nbase);
+    qf_item<CQ_LAYOUT_V>(v, item - per, n, S, vcodes, vscale, vminv, wv, sm, nx, nbase, &pf);
+    have = nx != nullptr && (item - per) % S != 0;
   }
 }
 
