@@ -86,3 +86,19 @@ def test_pair_long_context_headline():
         for x, words, layout in ((K, kc, "K"), (V, vc, "V")):
             c, sc, mn, _ = oracle.quantize_unit(x[b, h].cpu().numpy(), 1)
             assert np.array_equal(words_u32(words[b, h]), oracle.pack(c, 1, layout))
+
+
+@pytest.mark.parametrize("B,H,n", [(64, 8, 1000), (32, 8, 3328)])
+def test_pair_several_rounds_ragged(B, H, n):
+    """More items than workgroups and a ragged last chunk: workgroups walk
+    several items each, the K items hand over to V items inside a workgroup,
+    and the half of a next item requested during a rendezvous includes
+    rows clamped at the segment's end."""
+    K, V, *_ = draw_inputs(B, 4 * H, H, n, 0, seed=n + 17, host=False)
+    note(f"quantize pair several rounds B={B} H={H} n={n}")
+    (kc, ks, km), (vc, vs, vm) = _pair_vs_single(K, V, 1, ws_fill=9)
+    for b, h in ((0, 1), (B // 2, 3), (B - 1, H - 1)):
+        for x, words, scale, layout in ((K, kc, ks, "K"), (V, vc, vs, "V")):
+            c, sc, mn, _ = oracle.quantize_unit(x[b, h].cpu().numpy(), 1)
+            assert np.array_equal(words_u32(words[b, h]), oracle.pack(c, 1, layout))
+            assert np.array_equal(scale[b, h].cpu().numpy().view(np.uint32), sc.view(np.uint32))
