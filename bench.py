@@ -32,8 +32,12 @@ Sweeps (not the headline line; one JSON line per point, then a table):
                            quantization.  No name: all four
 
 Profiling helpers (used to produce profiles/):
-    --only {step,copy}     run only the timed steps, or only a 1 GiB copy
-                           kernel (the HBM-counter calibration reference)
+    --only {step,decode,copy}
+                           run only the timed steps, only the decode
+                           (--steps calls on the quantized cache, with
+                           --path choosing the decode schedule), or only a
+                           1 GiB copy kernel (the HBM-counter calibration
+                           reference)
     --summarize DIR ...    turn rocprofv3 CSV output dirs into profiles/ files
 """
 from __future__ import annotations
@@ -215,7 +219,7 @@ def run(args):
 
     # preallocated outputs and workspaces: the timed loop allocates nothing
     (kc, ks, km), (vc, vs, vm) = cqb.cq_quantize_kv_pair(K, V, cfg.bits)
-    qws = torch.empty(max(1, cqb.lib.cq_quantize_kv_pair_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
+    qws = torch.zeros(max(256, cqb.lib.cq_quantize_kv_pair_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
                       dtype=torch.uint8, device=dev)
     dws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d,
                                                               cfg.bits)), dtype=torch.uint8, device=dev)
@@ -224,9 +228,25 @@ def run(args):
     def quant():
         cqb.cq_quantize_kv_pair(K, V, cfg.bits, k_out=(kc, ks, km), v_out=(vc, vs, vm), workspace=qws)
 
-    def decode():
+    def decode(path=cqb.CQ_PATH_AUTO):
         cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=cfg.bits, sm_scale=sm,
-                           calib=calib, out=out, workspace=dws)
+                           calib=calib, out=out, workspace=dws, path=path)
+
+    if args.only == "decode":
+        path = getattr(cqb, "CQ_PATH_" + args.path.upper())
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        for _ in range(args.warmup):
+            decode(path)
+        torch.cuda.synchronize()
+        ev[0].record(stream)
+        for k in range(args.steps):
+            decode(path)
+            ev[k + 1].record(stream)
+        torch.cuda.synchronize()
+        ts = [ev[k].elapsed_time(ev[k + 1]) for k in range(args.steps)]
+        print(json.dumps({"workload": cfg.name, "path": args.path, "calls": args.steps,
+                          "decode_ms_median": float(np.median(ts))}), flush=True)
+        return
 
     for _ in range(args.warmup):
         quant()
@@ -249,6 +269,12 @@ def run(args):
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    # every quantize call completed its waits (else its codes would be
+    # invalid): the last call's status word, and the header word that any
+    # timed-out call since the workspace was zeroed sets
+    cqb.cq_quantize_status(qws)
+    if int(qws[4:8].view(torch.int32).item()) != 0:
+        raise RuntimeError("a quantize call of the run timed out waiting; its codes were invalid")
     tq = np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]) * 1e-3
     td = np.mean([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]) * 1e-3
     print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
@@ -644,7 +670,9 @@ def main():
     ap.add_argument("--workload", default="long_n8192")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--only", choices=["step", "copy"], default=None)
+    ap.add_argument("--only", choices=["step", "decode", "copy"], default=None)
+    ap.add_argument("--path", default="auto", choices=["auto", "fast", "fast_one", "fast_lds", "fast_split", "generic"],
+                    help="decode schedule for --only decode")
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
     ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream"], default=None)
     ap.add_argument("--command-note", default="")

@@ -26,7 +26,7 @@ import torch  # noqa: E402,F401
 
 lib = ctypes.CDLL(LIB_PATH)
 
-CQ_OK, CQ_ERR_INVALID_ARG, CQ_ERR_UNSUPPORTED, CQ_ERR_WORKSPACE, CQ_ERR_HIP = range(5)
+CQ_OK, CQ_ERR_INVALID_ARG, CQ_ERR_UNSUPPORTED, CQ_ERR_WORKSPACE, CQ_ERR_HIP, CQ_ERR_TIMEOUT = range(6)
 CQ_F16, CQ_F32 = 0, 1
 CQ_LAYOUT_K, CQ_LAYOUT_V = 0, 1
 CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT, CQ_PATH_FAST_LDS = 0, 1, 2, 3, 4, 5
@@ -34,7 +34,7 @@ CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLI
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
             "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16", "cq_kv_range_update",
-            "cq_quantize_kv_rows", "cq_quantize_kv_pair_workspace", "cq_quantize_kv_pair")
+            "cq_quantize_kv_rows", "cq_quantize_kv_pair_workspace", "cq_quantize_kv_pair", "cq_quantize_status")
 
 
 class cq_calib(ctypes.Structure):
@@ -43,7 +43,7 @@ class cq_calib(ctypes.Structure):
 
 
 class cq_opts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("splits", ctypes.c_int32)]
+    _fields_ = [("path", ctypes.c_int32), ("splits", ctypes.c_int32), ("max_polls", ctypes.c_int32)]
 
 
 _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -63,6 +63,8 @@ lib.cq_quantize_kv_pair_workspace.restype = _sz
 lib.cq_quantize_kv_pair_workspace.argtypes = [_i32] * 5
 lib.cq_quantize_kv_pair.restype = _i32
 lib.cq_quantize_kv_pair.argtypes = [_vp, _vp, _i32] + [_i32] * 5 + [_vp] * 6 + [_vp, _sz, ctypes.POINTER(cq_opts), _vp]
+lib.cq_quantize_status.restype = _i32
+lib.cq_quantize_status.argtypes = [_vp, _vp]
 lib.cq_kv_range_update.restype = _i32
 lib.cq_kv_range_update.argtypes = [_vp, _i32] + [_i32] * 6 + [_vp, _vp, _i32, _vp, _vp]
 lib.cq_quantize_kv_rows.restype = _i32
@@ -146,9 +148,19 @@ def code_words_shape(B, H, n, d, bits, layout):
     return (B, H, d // E, n) if layout == CQ_LAYOUT_K else (B, H, -(-n // E), d)
 
 
+def cq_quantize_status(workspace, device=None):
+    """Raise CQError(CQ_ERR_TIMEOUT) if the last quantize call on `workspace`
+    had a workgroup give up waiting (its outputs are then invalid).
+    Synchronizes the current stream of the workspace's device."""
+    _check(lib.cq_quantize_status(_ptr(workspace), _stream(device or workspace.device)), "cq_quantize_status")
+
+
 def cq_quantize_kv(x, bits: int, layout: int, codes=None, scale=None, minv=None, workspace=None,
-                   path: int = CQ_PATH_AUTO):
-    """x [B, H, n, d] float16/float32 -> (codes int32 words, scale f32 [B,H,d], minv f32 [B,H,d])."""
+                   path: int = CQ_PATH_AUTO, check: bool = False, max_polls: int = 0):
+    """x [B, H, n, d] float16/float32 -> (codes int32 words, scale f32 [B,H,d], minv f32 [B,H,d]).
+
+    check=True synchronizes and raises CQError(CQ_ERR_TIMEOUT) if a workgroup
+    gave up waiting (cq_quantize_status); max_polls is cq_opts.max_polls."""
     torch = _torch()
     _need(x, "x")
     B, H, n, d = x.shape
@@ -165,11 +177,13 @@ def cq_quantize_kv(x, bits: int, layout: int, codes=None, scale=None, minv=None,
     ws_bytes = lib.cq_quantize_kv_workspace(B, H, n, d, bits)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    opts = cq_opts(path, 0)
+    opts = cq_opts(path, 0, max_polls)
     st = lib.cq_quantize_kv(_ptr(x), _dtype_code(x), B, H, n, d, bits, layout, _ptr(codes), _ptr(scale),
                             _ptr(minv), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                             ctypes.byref(opts), _stream(dev))
     _check(st, "cq_quantize_kv")
+    if check and workspace is not None:
+        cq_quantize_status(workspace, dev)
     return codes, scale, minv
 
 
@@ -200,7 +214,7 @@ def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, 
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     c = make_calib(calib)
-    opts = cq_opts(path, splits)
+    opts = cq_opts(path, splits, 0)
     st = lib.cq_decode_attn(_ptr(q), _dtype_code(q), _ptr(k_codes) if n else None, _ptr(k_scale),
                             _ptr(k_min), _ptr(v_codes) if n else None, _ptr(v_scale), _ptr(v_min),
                             _ptr(k_tail) if T else None, _ptr(v_tail) if T else None, tail_code,
@@ -285,10 +299,12 @@ def cq_decode_attn_fp16(q, k, v, sm_scale: float, out=None, workspace=None):
     return out
 
 
-def cq_quantize_kv_pair(k, v, bits: int, k_out=None, v_out=None, workspace=None, path: int = CQ_PATH_AUTO):
+def cq_quantize_kv_pair(k, v, bits: int, k_out=None, v_out=None, workspace=None, path: int = CQ_PATH_AUTO,
+                        check: bool = False, max_polls: int = 0):
     """One layer's K and V [B, H, n, d] (same shape and dtype) quantized in one
     call.  Returns ((k_codes, k_scale, k_min), (v_codes, v_scale, v_min)) in
-    the K and V layouts; k_out / v_out may pass those buffers."""
+    the K and V layouts; k_out / v_out may pass those buffers.  check and
+    max_polls as for cq_quantize_kv."""
     torch = _torch()
     _need(k, "k")
     _need(v, "v", tuple(k.shape), k.dtype, k.device)
@@ -310,11 +326,13 @@ def cq_quantize_kv_pair(k, v, bits: int, k_out=None, v_out=None, workspace=None,
     ws_bytes = lib.cq_quantize_kv_pair_workspace(B, H, n, d, bits)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
-    opts = cq_opts(path, 0)
+    opts = cq_opts(path, 0, max_polls)
     st = lib.cq_quantize_kv_pair(_ptr(k), _ptr(v), _dtype_code(k), B, H, n, d, bits, _ptr(kc), _ptr(ks), _ptr(km),
                                  _ptr(vc), _ptr(vs), _ptr(vm), _ptr(workspace),
                                  0 if workspace is None else workspace.numel(), ctypes.byref(opts), _stream(dev))
     _check(st, "cq_quantize_kv_pair")
+    if check and workspace is not None:
+        cq_quantize_status(workspace, dev)
     return (kc, ks, km), (vc, vs, vm)
 
 

@@ -40,7 +40,9 @@ class QuantizedVisualKV:
         if k_visual.shape != v_visual.shape:
             raise ValueError(f"K {tuple(k_visual.shape)} and V {tuple(v_visual.shape)} differ")
         self.B, self.Hkv, self.n, self.d = k_visual.shape
-        self.k, self.v = cq_quantize_kv_pair(k_visual, v_visual, bits)   # each (codes, scale, min)
+        # each (codes, scale, min); check=True synchronizes once and raises if a
+        # workgroup of the fused quantizer gave up waiting (invalid codes)
+        self.k, self.v = cq_quantize_kv_pair(k_visual, v_visual, bits, check=True)
 
     @classmethod
     def from_codes(cls, k, v, n: int, bits: int) -> "QuantizedVisualKV":

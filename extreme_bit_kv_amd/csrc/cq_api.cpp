@@ -17,6 +17,7 @@ bool valid_dtype(int32_t t) { return t == CQ_F16 || t == CQ_F32; }
 bool al16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 bool al4(const void* p) { return ((uintptr_t)p & 3u) == 0; }
 int opt_path(const cq_opts* o) { return o ? o->path : CQ_PATH_AUTO; }
+long opt_polls(const cq_opts* o) { return o ? (long)o->max_polls : 0L; }
 
 thread_local int32_t g_last_hip_error = 0;
 
@@ -55,6 +56,7 @@ const char* cq_status_str(cq_status s) {
     case CQ_ERR_UNSUPPORTED: return "CQ_ERR_UNSUPPORTED: valid arguments not supported by this build";
     case CQ_ERR_WORKSPACE: return "CQ_ERR_WORKSPACE: workspace missing or too small";
     case CQ_ERR_HIP: return "CQ_ERR_HIP: HIP runtime call failed";
+    case CQ_ERR_TIMEOUT: return "CQ_ERR_TIMEOUT: a quantize workgroup gave up waiting; its outputs are invalid";
   }
   return "unknown cq_status";
 }
@@ -75,7 +77,7 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
     return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (scale == nullptr || minv == nullptr) return CQ_ERR_INVALID_ARG;
@@ -83,7 +85,8 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
     if (!al16(x) || !al16(codes) || !al4(scale) || !al4(minv) || !al16(workspace)) return CQ_ERR_INVALID_ARG;
   }
   if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
-  cqi::QuantArgs a{x, x_dtype, B, H, n, d, bits, layout, codes, scale, minv, workspace, (hipStream_t)stream};
+  cqi::QuantArgs a{x, x_dtype, B, H, n, d, bits, layout, codes, scale, minv, workspace, (hipStream_t)stream,
+                   opt_polls(opts), 1};
   const bool fused_ok = cqi::quant_fused_supported(a);
   if (path >= CQ_PATH_FAST && !fused_ok) return CQ_ERR_UNSUPPORTED;
   const bool use_fused = fused_ok && path != CQ_PATH_GENERIC;
@@ -108,7 +111,7 @@ cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, in
   if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype)) return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (k_scale == nullptr || k_min == nullptr || v_scale == nullptr || v_min == nullptr) return CQ_ERR_INVALID_ARG;
@@ -119,9 +122,10 @@ cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, in
   }
   if (d != cqi::kHeadDim) return CQ_ERR_UNSUPPORTED;
   cqi::QuantArgs ka{k, x_dtype, B, H, n, d, bits, CQ_LAYOUT_K, k_codes, k_scale, k_min, workspace,
-                    (hipStream_t)stream};
+                    (hipStream_t)stream, opt_polls(opts), 1};
+  // the V tensor, run after K on the same workspace, keeps K's status word
   cqi::QuantArgs va{v, x_dtype, B, H, n, d, bits, CQ_LAYOUT_V, v_codes, v_scale, v_min, workspace,
-                    (hipStream_t)stream};
+                    (hipStream_t)stream, opt_polls(opts), 0};
   const bool pair_ok = cqi::quant_fused_pair_supported(ka) && path != CQ_PATH_GENERIC;
   if (pair_ok) {
     const size_t need = cqi::quant_fused_pair_ws(B, H, n, d);
@@ -139,6 +143,16 @@ cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, in
   const hipError_t e = use_fused ? cqi::quant_fused(ka) : cqi::quant_generic(ka);
   if (e != hipSuccess) return from_hip(e);
   return from_hip(use_fused ? cqi::quant_fused(va) : cqi::quant_generic(va));
+}
+
+cq_status cq_quantize_status(const void* workspace, void* stream) {
+  if (workspace == nullptr || !al16(workspace)) return CQ_ERR_INVALID_ARG;
+  clear_stale_hip_error();
+  int32_t word = 0;
+  hipError_t e = hipMemcpyAsync(&word, workspace, sizeof(word), hipMemcpyDeviceToHost, (hipStream_t)stream);
+  if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return from_hip(e);
+  return word == 0 ? CQ_OK : CQ_ERR_TIMEOUT;
 }
 
 // ---------------------------------------------------------------------------

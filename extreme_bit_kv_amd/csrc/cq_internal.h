@@ -30,9 +30,12 @@ struct QuantArgs {
   uint32_t* codes;
   float* scale;
   float* minv;
-  void* ws;
+  void* ws;             // first kWsHeader bytes: the status word, then the path's own data
   hipStream_t stream;
+  long spin_limit = 0;  // fused path: unsuccessful polls before giving up; 0 = default
+  int reset_status = 1; // 0: keep the status word (the second tensor of a pair)
 };
+constexpr size_t kWsHeader = 256;   // quantization workspace header (status word at offset 0)
 size_t quant_generic_ws(int B, int H, int n, int d);
 hipError_t quant_generic(const QuantArgs& a);
 

@@ -38,19 +38,33 @@ __device__ __forceinline__ v4i spread_hi(uint32_t w) {
 
 // 1-bit words masked in place, one AND per register: element e (at bit
 // 8 (e mod 4) + floor(e / 4)) is left in byte e mod 4 of register
-// floor(e / 4) mod 4 as c_e 2^s(e), s(e) = min(floor(e / 4), 6).  The top bit
-// of each byte is moved down one place so that every byte is a non-negative
-// int8.  The other operand of the product carries 2^(7 - s(e)) for element e
-// (see bit_weight), so every product comes out as 2^7 c_e times its factor.
+// floor(e / 4) mod 4 as c_e 2^s(e), s(e) = floor(e / 4) mod 4.  bits_lo
+// takes elements 0..15 straight from the word; bits_hi takes elements 16..31
+// from the word shifted down by 4 (bits 4..7 of each byte move to bits 0..3
+// of the same byte), so every byte is a code bit of weight 1, 2, 4 or 8.  The
+// other operand of the product carries 2^(3 - s(e)) for element e (see
+// bit_weight), so every product comes out as 2^3 c_e times its factor.
 __device__ __forceinline__ v4i bits_lo(uint32_t w) {
   return v4i{(int)(w & 0x01010101u), (int)(w & 0x02020202u), (int)(w & 0x04040404u), (int)(w & 0x08080808u)};
 }
 __device__ __forceinline__ v4i bits_hi(uint32_t w) {
-  return v4i{(int)(w & 0x10101010u), (int)(w & 0x20202020u), (int)(w & 0x40404040u),
-             (int)((w >> 1) & 0x40404040u)};
+  const uint32_t x = w >> 4;
+  return v4i{(int)(x & 0x01010101u), (int)(x & 0x02020202u), (int)(x & 0x04040404u), (int)(x & 0x08080808u)};
 }
-// log2 of the compensating factor of element e of a word: 7 - s(e)
-__device__ __forceinline__ int bit_weight(int e) { return 7 - min((e >> 2) & 7, 6); }
+// log2 of the compensating factor of element e of a word: 3 - s(e)
+__device__ __forceinline__ int bit_weight(int e) { return 3 - ((e >> 2) & 3); }
+
+// Probability p in [0, 1] (up to rounding) as the fixed-point integer
+// P = round(p 2^27): float32 keeps 24 significant bits of p, so P is p to
+// 2^-24 relative, and to 2^-28 absolute below 2^-4.  A p slightly above 1
+// from rounding gives P slightly above 2^27, which every user tolerates.
+constexpr float kPOne = 134217728.f;          // 2^27
+__device__ __forceinline__ uint32_t p_fixed(float p) { return (uint32_t)fmaf(p, kPOne, 0.5f); }
+
+// Four signed base-256 digits of |x| < 2^30: the bytes of x + 0x808080 with
+// the low three offset back by 128, so x = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3
+// with every d_k a signed byte.
+__device__ __forceinline__ uint32_t sdigits(uint32_t x) { return (x + 0x00808080u) ^ 0x00808080u; }
 
 // 4 x 4 byte transpose: o_p holds byte p of f0, f1, f2, f3 (in that order)
 __device__ __forceinline__ void transpose_bytes(uint32_t f0, uint32_t f1, uint32_t f2, uint32_t f3,

@@ -119,7 +119,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // V-side A digits: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_ptail[4];
+  __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
   __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
   __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
@@ -225,7 +225,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     int F = 0;
     if (mq > 0.f) F = 21 - ilogbf(mq);
     s_F[tid] = F;
-    s_inv2f[tid] = ldexpf(1.f, -F - 7);         // products carry 2^7 (bits_lo / bits_hi)
+    s_inv2f[tid] = ldexpf(1.f, -F - 3);         // products carry 2^3 (bits_lo / bits_hi)
     s_c0[tid] = c0;
   }
   lds_barrier();
@@ -235,7 +235,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     // Qs + 0x808080 with the low three offset back by 128 (signed base-256)
     const int hh = tid >> 7, j = tid & 127;
     const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
-    const uint32_t dig = ((uint32_t)(Q * (1 << bit_weight(j & 31))) + 0x00808080u) ^ 0x00808080u;   // |Qs| <= 2^29
+    const uint32_t dig = cqm::sdigits((uint32_t)(Q * (1 << bit_weight(j & 31))));   // |Q 2^wt| <= 2^25
     unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
 #pragma unroll
     for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + j] = (unsigned char)(dig >> (8 * pl));
@@ -307,7 +307,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       v4i acc = {0, 0, 0, 0};
       acc = mfma(ak0, bits_lo(wd[m]), acc);
       acc = mfma(ak1, bits_hi(wd[m]), acc);
-      // 2^7 Q . c = lo + 2^16 hi; both halves fit 31 bits, the sum is
+      // 2^3 Q . c = lo + 2^16 hi; both halves fit 31 bits, the sum is
       // rounded to float (the same operations in both passes)
       const int lo = acc[0] + (acc[1] << 8), hi = acc[2] + (acc[3] << 8);
       st[m] = fmaf(fmaf((float)hi, 65536.f, (float)lo), inv2f, c0f);
@@ -408,12 +408,17 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
       lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
       mu = t_lo - lam * m;
-      vis_max = fmaxf(t_lo, t_hi);
+      // the largest value of g: the larger end of [t_lo, t_hi], or t_lo
+      // when every score is the same (g is then the constant t_lo)
+      vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
     }
     const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
     if (lane == 0) {
-      s_lam[hh] = lam * kLog2e;                 // p = 2^(s * lam' + mu')
-      s_mu[hh] = (mu - top) * kLog2e;
+      // visual weights relative to the largest one: p = 2^(s * lam' + mu');
+      // alpha = its weight relative to the softmax reference
+      s_lam[hh] = lam * kLog2e;
+      s_mu[hh] = (mu - vis_max) * kLog2e;
+      s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
     }
     // tail probabilities (in place) and their sum
     float pt = 0.f;
@@ -475,8 +480,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   v4i vacc[8];
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) vacc[ct] = v4i{0, 0, 0, 0};
-  // the wave's int32 plane sums grow by at most 2^20 per tile (128 tokens x
-  // |digit| <= 128 x code byte <= 64); they are moved into the exact 64-bit
+  // the wave's int32 plane sums grow by at most 2^17 per tile (128 tokens x
+  // |digit| <= 128 x code byte <= 8); they are moved into the exact 64-bit
   // LDS sums every kFlushTiles tiles, far below 2^31
   constexpr int kFlushTiles = 256;
   auto flush = [&]() {
@@ -501,9 +506,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
     load_k(nxt, kn0, kn1);
     load_v(nxt, vn0, vn1);
-    // probabilities of this lane's 8 tokens (head oh) as 22-bit fixed point
-    // P = round(p 2^22), the mantissa of p 2^22 + 2^23; tokens that do not
-    // count get exponent -inf, so p = 0
+    // probabilities of this lane's 8 tokens (head oh), relative to the
+    // largest calibrated visual score, as fixed point P = round(p 2^27);
+    // tokens that do not count get exponent -inf, so p = 0
     const bool ok = oh < G && tile * kTile + 8 * i16 < n;
     const float mu_t = ok ? mu2 : -INFINITY;
     float st[8];
@@ -512,10 +517,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const float p = __builtin_amdgcn_exp2f(fmaf(st[m], lam2, mu_t));   // argument <= 0 (up to rounding)
-      const uint32_t Pm = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) & 0x007FFFFFu;
+      const uint32_t Pm = cqm::p_fixed(p);
       ptile += Pm;
-      // digits of P 2^wt: bytes of P 2^wt + 0x808080, the low three offset back by 128
-      fb[m] = ((Pm << (m < 4 ? wt0 : wt1)) + 0x00808080u) ^ 0x00808080u;
+      fb[m] = cqm::sdigits(Pm << (m < 4 ? wt0 : wt1));   // digits of P 2^wt, |P 2^wt| <= 2^30
     }
     psum += (double)ptile;
     if (oh < G) {
@@ -560,15 +564,18 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   lds_barrier();
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
-    const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 536870912.0));   // 2^-29
-    const float pv = (float)(s_psum[hh] * (1.0 / 4194304.0));
+    const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 1073741824.0));   // 2^-30
+    const float pv = (float)(s_psum[hh] * (1.0 / 134217728.0));                       // 2^-27
     float tail = 0.f;
 #pragma unroll
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
     const float pt = s_ptail[hh];
+    // the visual sums are relative to the largest visual probability,
+    // alpha = exp(visual max - softmax max) relative to the reference
+    const float al = s_alpha[hh];
     float o = tail;
-    if (n > 0) o += s_vs[j] * sv + pv * s_vm[j];
-    o /= (pv + pt);
+    if (n > 0) o += al * (s_vs[j] * sv + pv * s_vm[j]);
+    o /= (al * pv + pt);
     const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
     if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
     else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);
@@ -613,7 +620,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
   __shared__ __align__(16) uint32_t s_adig[4][4][32];
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWavesL][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_ptail[4];
+  __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
   __shared__ float s_tailred[kThreads / 64][4][128];   // df_b1's eight token phases
   __shared__ unsigned long long s_vsum[4][128];
   __shared__ double s_psum[4];
@@ -741,14 +748,14 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       int F = 0;
       if (mq > 0.f) F = 21 - ilogbf(mq);
       s_F[tid] = F;
-      s_inv2f[tid] = ldexpf(1.f, -F - 7);
+      s_inv2f[tid] = ldexpf(1.f, -F - 3);
       s_c0[tid] = c0;
     }
     lds_barrier();
     if (tid < 512) {
       const int hh = tid >> 7, j = tid & 127;
       const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));
-      const uint32_t dig = ((uint32_t)(Q * (1 << bit_weight(j & 31))) + 0x00808080u) ^ 0x00808080u;
+      const uint32_t dig = cqm::sdigits((uint32_t)(Q * (1 << bit_weight(j & 31))));
       unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
 #pragma unroll
       for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + j] = (unsigned char)(dig >> (8 * pl));
@@ -905,12 +912,13 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
         const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
         lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
         mu = t_lo - lam * m;
-        vis_max = fmaxf(t_lo, t_hi);
+        vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
       }
       const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
       if (lane == 0) {
         s_lam[hh] = lam * kLog2e;
-        s_mu[hh] = (mu - top) * kLog2e;
+        s_mu[hh] = (mu - vis_max) * kLog2e;
+        s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
       }
       float ptl = 0.f;
       for (int j = lane; j < T; j += 64) {
@@ -1005,9 +1013,9 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
         const float p = __builtin_amdgcn_exp2f(fmaf(st[m], lam2, mu_t));
-        const uint32_t Pm = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) & 0x007FFFFFu;
+        const uint32_t Pm = cqm::p_fixed(p);
         ptile += Pm;
-        fb[m] = ((Pm << (m < 4 ? wt0 : wt1)) + 0x00808080u) ^ 0x00808080u;
+        fb[m] = cqm::sdigits(Pm << (m < 4 ? wt0 : wt1));
       }
       psum += (double)ptile;
       wave_sync_lds();                          // every lane has read its scores of the tile
@@ -1067,15 +1075,16 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
     lds_barrier();
     if (tid < G * 128) {
       const int hh = tid >> 7, j = tid & 127;
-      const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 536870912.0));
-      const float pv = (float)(s_psum[hh] * (1.0 / 4194304.0));
+      const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 1073741824.0));
+      const float pv = (float)(s_psum[hh] * (1.0 / 134217728.0));
       float tail = 0.f;
 #pragma unroll
       for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
       const float ptt = s_ptail[hh];
+      const float al = s_alpha[hh];
       float o = tail;
-      if (n > 0) o += s_vs[j] * sv + pv * s_vm[j];
-      o /= (pv + ptt);
+      if (n > 0) o += al * (s_vs[j] * sv + pv * s_vm[j]);
+      o /= (al * pv + ptt);
       const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
       if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
       else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);
@@ -1116,10 +1125,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
   __shared__ __align__(16) uint32_t s_adig[4][3][32];
-  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][TB / 4];   // V-side A digits: [head][plane][TB bytes]
+  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][TB / 4];   // V-side A digits: [head][plane][TB bytes]
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWaves][4][2];
-  __shared__ float s_lam[4], s_mu[4], s_ptail[4];
+  __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
   __shared__ float s_tailred[kThreads / 64][4][128];
   __shared__ float s_vred[kWaves][4][128];
   __shared__ float s_psum[kWaves][4];
@@ -1385,12 +1394,17 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
       lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
       mu = t_lo - lam * m;
-      vis_max = fmaxf(t_lo, t_hi);
+      // the largest value of g: the larger end of [t_lo, t_hi], or t_lo
+      // when every score is the same (g is then the constant t_lo)
+      vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
     }
     const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
     if (lane == 0) {
-      s_lam[hh] = lam * kLog2e;                 // p = 2^(s * lam' + mu')
-      s_mu[hh] = (mu - top) * kLog2e;
+      // visual weights relative to the largest one: p = 2^(s * lam' + mu');
+      // alpha = its weight relative to the softmax reference
+      s_lam[hh] = lam * kLog2e;
+      s_mu[hh] = (mu - vis_max) * kLog2e;
+      s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
     }
     // tail probabilities (in place) and their sum
     float pt = 0.f;
@@ -1462,6 +1476,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     if constexpr (BITS < 8) load_k(tile + kWaves, kn);
     load_v(tile + kWaves, vn);
     const bool ok = oh < G && tile * TB + TPL * i16 < n;
+    // p relative to the largest visual probability, as four signed digits of
+    // P = round(p 2^27)
     uint32_t fb[TPL];
 #pragma unroll
     for (int m = 0; m < TPL; ++m) {
@@ -1469,13 +1485,13 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       float p = 0.f;
       if (ok) p = exp2f(fmaf(s, lam2, mu2));
       psum += p;
-      fb[m] = __float_as_uint(fmaf(p, 4194304.f, 8388608.f)) ^ 0x00008080u;   // bytes: P^0x80, (P>>8)^0x80, P>>16
+      fb[m] = cqm::sdigits(cqm::p_fixed(p));
     }
     if constexpr (BITS == 8) load_k(tile + kWaves, kn);
     if (oh < G) {
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
-        unsigned char* dst = pd + (oh * 3 + pl) * TB + TPL * i16;
+      for (int pl = 0; pl < 4; ++pl) {
+        unsigned char* dst = pd + (oh * 4 + pl) * TB + TPL * i16;
         if constexpr (TPL == 4) {
           *reinterpret_cast<uint32_t*>(dst) = gather_byte(fb[0], fb[1], fb[2], fb[3], pl);
         } else {
@@ -1486,10 +1502,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     }
     wave_sync_lds();
     v4i av = {0, 0, 0, 0};
-    if (rp == 3) {
-      av = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-    } else if (rh < G) {
-      const unsigned char* src = pd + (rh * 3 + rp) * TB + E * g4;
+    if (rh < G) {
+      const unsigned char* src = pd + (rh * 4 + rp) * TB + E * g4;
       if constexpr (E == 16) {
         const uint4 x = *reinterpret_cast<const uint4*>(src);
         av = v4i{(int)x.x, (int)x.y, (int)x.z, (int)x.w};
@@ -1522,10 +1536,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   // lane (head oh, column i16): channels 8*i16 + ct
 #pragma unroll
   for (int ct = 0; ct < 8; ++ct) {
-    const float cnt128 = 128.f * (float)vacc[ct][3];
-    const float sv = ((float)vacc[ct][0] + cnt128) + 256.f * ((float)vacc[ct][1] + cnt128) +
-                     65536.f * (float)vacc[ct][2];
-    s_vred[wave][oh][8 * i16 + ct] = sv * (1.f / 4194304.f);
+    const long long sv = (long long)vacc[ct][0] + 256ll * vacc[ct][1] + 65536ll * vacc[ct][2] +
+                         16777216ll * vacc[ct][3];
+    s_vred[wave][oh][8 * i16 + ct] = (float)((double)sv * (1.0 / 134217728.0));   // 2^-27
   }
 #pragma unroll
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
@@ -1542,10 +1555,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     float tail = 0.f;
 #pragma unroll
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
-    const float pt = s_ptail[hh];
+    const float pt = s_ptail[hh], al = s_alpha[hh];
     float o = tail;
-    if (n > 0) o += P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j];
-    o /= (pv + pt);
+    if (n > 0) o += al * (P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j]);
+    o /= (al * pv + pt);
     const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
     if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
     else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);

@@ -150,7 +150,7 @@ __global__ void __launch_bounds__(kThreads) dg_attend(Shape sh, CalibP cal, cons
         float l = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
         lam[g] = l;
         mu[g] = t_lo - l * m;
-        shift[g] = fmaxf(t_lo, t_hi);
+        shift[g] = M > m ? fmaxf(t_lo, t_hi) : t_lo;    // the largest value of g
       } else {
         lam[g] = 1.f;
         mu[g] = 0.f;

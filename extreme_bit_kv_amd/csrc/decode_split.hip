@@ -365,8 +365,10 @@ __global__ void __launch_bounds__(kThreads, 4) ds_keys(SParams P) {
 }
 
 // ---- launch 2: value pass ---------------------------------------------------
-// Record c < nc of a unit: the visual chunk c (sum_i P_i c_i / 2^22 per
-// channel, then sum_i p_i).  Record nc, written by chunk 0: the text tail
+// Record c < nc of a unit: the visual chunk c (alpha sum_i P_i c_i / 2^27 per
+// channel, then alpha sum_i P_i / 2^27, with P_i the fixed-point weight of
+// token i relative to the largest visual one and alpha that one's weight
+// relative to the softmax reference).  Record nc, written by chunk 0: the text tail
 // (sum_j p_j vt_j per channel, then sum_j p_j).
 template <int G, bool F32, int MT>
 __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
@@ -376,10 +378,10 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   const int n = P.n, T = P.T, ntiles = (n + kTile - 1) / kTile, R = n >> 5;
   const int i16 = lane & 15, g4 = lane >> 4, rh = i16 >> 2, rp = i16 & 3, oh = lane >> 4;
   __shared__ QSmem qs;
-  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][3][32];   // [head][plane][128 token bytes]
-  __shared__ unsigned long long s_vsum[4][128];   // sum P c per head and channel (2^-22 units)
-  __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
-  __shared__ float s_lam[4], s_mu[4], s_top[4];
+  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // [head][plane][128 token bytes]
+  __shared__ unsigned long long s_vsum[4][128];   // sum P c per head and channel (2^-27 units)
+  __shared__ double s_psum[4];                     // sum P per head (2^-27 units)
+  __shared__ float s_lam[4], s_mu[4], s_top[4], s_alpha[4];
   if (tid < 4) s_psum[tid] = 0.0;
   for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
@@ -417,13 +419,16 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
       const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
       lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
       mu = t_lo - lam * m;
-      vis_max = fmaxf(t_lo, t_hi);
+      // the largest value of g: the larger end of [t_lo, t_hi], or t_lo
+      // when every score is the same (g is then the constant t_lo)
+      vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
     }
     const float top = fmaxf(vis_max, tmax);
     if (lane == 0) {
-      s_lam[hh] = lam * kLog2e;                 // p = 2^(s lam' + mu')
-      s_mu[hh] = (mu - top) * kLog2e;
+      s_lam[hh] = lam * kLog2e;                 // p / p_max = 2^(s lam' + mu')
+      s_mu[hh] = (mu - vis_max) * kLog2e;
       s_top[hh] = top;
+      s_alpha[hh] = exp2f((vis_max - top) * kLog2e);
     }
   }
   lds_barrier();                                // the first tiles stay in flight
@@ -448,42 +453,34 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
     const bool okB = oh < G && tile * kTile + tok_of(i16, 4) < n;
     float st[8];
     tile_scores(ko, kw0, kw1, st);
-    // P = round(p 2^22): the mantissa of p 2^22 + 2^23
+    // P = round(p 2^27) as four signed base-256 digits
     uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       float p = 0.f;
       if (m < 4 ? okA : okB) p = exp2f(fmaf(st[m], lam2, mu2));
-      const uint32_t f = __float_as_uint(fmaf(p, 4194304.f, 8388608.f));
-      ptile += f & 0x007FFFFFu;
-      fb[m] = f ^ 0x00008080u;                   // bytes: P^0x80, (P>>8)^0x80, P>>16
+      const uint32_t Pm = cqm::p_fixed(p);
+      ptile += Pm;
+      fb[m] = cqm::sdigits(Pm);
     }
     psum += (double)ptile;
     if (oh < G) {
 #pragma unroll
-      for (int pl = 0; pl < 3; ++pl) {
+      for (int pl = 0; pl < 4; ++pl) {
         // token order within the tile: tokens 4 i16 .. +3, then 64 + 4 i16 .. +3
-        *reinterpret_cast<uint32_t*>(pd + (oh * 3 + pl) * 128 + tok_of(i16, 0)) =
+        *reinterpret_cast<uint32_t*>(pd + (oh * 4 + pl) * 128 + tok_of(i16, 0)) =
             gather_byte(fb[0], fb[1], fb[2], fb[3], pl);
-        *reinterpret_cast<uint32_t*>(pd + (oh * 3 + pl) * 128 + tok_of(i16, 4)) =
+        *reinterpret_cast<uint32_t*>(pd + (oh * 4 + pl) * 128 + tok_of(i16, 4)) =
             gather_byte(fb[4], fb[5], fb[6], fb[7], pl);
       }
     }
     wave_sync_lds();
-    v4i av0, av1;
-    if (rp < 3) {
-      if (rh < G) {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(pd + (rh * 3 + rp) * 128 + 32 * g4);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(pd + (rh * 3 + rp) * 128 + 32 * g4 + 16);
-        av0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-        av1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
-      } else {
-        av0 = v4i{0, 0, 0, 0};
-        av1 = av0;
-      }
-    } else {                                    // count row: restores the -128 digit offsets
-      av0 = v4i{0x01010101, 0x01010101, 0x01010101, 0x01010101};
-      av1 = av0;
+    v4i av0 = {0, 0, 0, 0}, av1 = {0, 0, 0, 0};
+    if (rh < G) {
+      const uint4 x0 = *reinterpret_cast<const uint4*>(pd + (rh * 4 + rp) * 128 + 32 * g4);
+      const uint4 x1 = *reinterpret_cast<const uint4*>(pd + (rh * 4 + rp) * 128 + 32 * g4 + 16);
+      av0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
+      av1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
     }
     const uint32_t vwd[8] = {vw0.x, vw0.y, vw0.z, vw0.w, vw1.x, vw1.y, vw1.z, vw1.w};
 #pragma unroll
@@ -500,9 +497,8 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   if (oh < G) {
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) {
-      const long long cnt128 = 128ll * vacc[ct][3];
-      const long long sv = ((long long)vacc[ct][0] + cnt128) + 256ll * ((long long)vacc[ct][1] + cnt128) +
-                           65536ll * (long long)vacc[ct][2];
+      const long long sv = (long long)vacc[ct][0] + 256ll * vacc[ct][1] + 65536ll * vacc[ct][2] +
+                           16777216ll * vacc[ct][3];
       atomicAdd(&s_vsum[oh][ch_of(i16, ct)], (unsigned long long)sv);
     }
   }
@@ -513,9 +509,9 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   float* rec = P.part + ((size_t)unit * (P.nc + 1) + chunk) * 4 * kPart;
   for (int idx = tid; idx < G * 128; idx += kThreads) {
     const int hh = idx >> 7, j = idx & 127;
-    rec[hh * kPart + j] = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 4194304.0));
+    rec[hh * kPart + j] = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 134217728.0) * s_alpha[hh]);
   }
-  if (tid < G) rec[tid * kPart + 128] = (float)(s_psum[tid] * (1.0 / 4194304.0));
+  if (tid < G) rec[tid * kPart + 128] = (float)(s_psum[tid] * (1.0 / 134217728.0) * s_alpha[tid]);
   if (chunk != 0) return;
 
   // ---- chunk 0: the text tail's record --------------------------------------

@@ -45,13 +45,14 @@ namespace {
 
 using namespace cqt;
 constexpr int kChunk = kTile;          // tokens per item (512)
-constexpr long kSpinLimit = 4000000;   // bounded wait (a few seconds); normal waits are microseconds
+constexpr long kSpinLimit = 4000000;   // default bounded wait (a few seconds); normal waits are microseconds
 
 constexpr uint32_t kEmpty = 0xFFFFFFFFu;
 constexpr int kGather = 4;             // chunk words a gathering thread loads at once
 
 struct Ws {
-  int* status;       // [0] time-out flag
+  int* status;       // [0] time-out flag of this call, [1] of any call since the caller zeroed it
+  long spin_limit;   // unsuccessful polls before a workgroup gives up
   uint32_t* slot;    // [units][S][128]: chunk range words (min16 | max16 << 16)
   uint32_t* fin;     // [units][128]: unit range words
 };
@@ -64,16 +65,19 @@ __host__ __device__ inline Ws carve(void* base, int units, int S) {
   char* p = (char*)base;
   Ws w;
   w.status = (int*)p;
+  w.spin_limit = kSpinLimit;
   w.slot = (uint32_t*)(p + 256);
   w.fin = w.slot + (size_t)units * S * 128;
   return w;
 }
 
-// slot and fin are contiguous, 16-byte aligned, a multiple of 128 words
-__global__ void qf_init(Ws w, long quads) {
+// slot and fin are contiguous, 16-byte aligned, a multiple of 128 words.
+// The status word is cleared unless this launch is the second tensor of a
+// pair quantized one after the other (the first one's time-out must stay).
+__global__ void qf_init(Ws w, long quads, int reset_status) {
   const long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < quads) reinterpret_cast<uint4*>(w.slot)[i] = make_uint4(kEmpty, kEmpty, kEmpty, kEmpty);
-  if (i == 0) w.status[0] = 0;
+  if (i == 0 && reset_status) w.status[0] = 0;
 }
 
 __device__ __forceinline__ void st_word(uint32_t* p, uint32_t v) {
@@ -190,8 +194,9 @@ __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int 
           }
           if (ready) break;
           __builtin_amdgcn_s_sleep(2);
-          if (++spins > kSpinLimit) {
+          if (++spins > w.spin_limit) {
             atomicExch(w.status, 1);
+            atomicExch(w.status + 1, 1);
             break;
           }
         }
@@ -220,8 +225,9 @@ __device__ __forceinline__ void qf_item(const uint4 (&v)[kRows], long item, int 
       long spins = 0;
       while ((uw = ld_word(w.fin + (size_t)u * 128 + tid)) == kEmpty) {
         __builtin_amdgcn_s_sleep(2);
-        if (++spins > kSpinLimit) {
+        if (++spins > w.spin_limit) {
           atomicExch(w.status, 1);
+          atomicExch(w.status + 1, 1);
           break;
         }
       }
@@ -366,8 +372,10 @@ hipError_t quant_fused_pair(const QuantArgs& k, const QuantArgs& v) {
   const int units = k.B * k.H;
   const int S = (k.n + kChunk - 1) / kChunk;
   Ws wk = carve(k.ws, units, S);
+  wk.spin_limit = k.spin_limit > 0 ? k.spin_limit : kSpinLimit;
   Ws wv;
   wv.status = wk.status;
+  wv.spin_limit = wk.spin_limit;
   wv.slot = wk.fin + (size_t)units * 128;
   wv.fin = wv.slot + (size_t)units * S * 128;
   const void* fn = (const void*)qf_b1_pair;
@@ -377,7 +385,7 @@ hipError_t quant_fused_pair(const QuantArgs& k, const QuantArgs& v) {
   const long items = 2L * units * S;
   if (grid > items) grid = items;
   const long quads = 2L * units * (S + 1) * 128 / 4;     // both tensors' words
-  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, k.stream, wk, quads);
+  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, k.stream, wk, quads, 1);
   const __half* xk = (const __half*)k.x;
   const __half* xv = (const __half*)v.x;
   int n = k.n, Sv = S, un = units;
@@ -390,6 +398,7 @@ hipError_t quant_fused(const QuantArgs& a) {
   const int units = a.B * a.H;
   const int S = (a.n + kChunk - 1) / kChunk;
   Ws w = carve(a.ws, units, S);
+  w.spin_limit = a.spin_limit > 0 ? a.spin_limit : kSpinLimit;
   const void* fn = a.layout == CQ_LAYOUT_K ? (const void*)qf_b1<CQ_LAYOUT_K> : (const void*)qf_b1<CQ_LAYOUT_V>;
   const long capacity = capacity_of(fn, a.layout == CQ_LAYOUT_K ? 0 : 1);
   if (capacity < S) return hipErrorInvalidConfiguration;
@@ -397,7 +406,7 @@ hipError_t quant_fused(const QuantArgs& a) {
   const long items = (long)units * S;
   if (grid > items) grid = items;
   const long quads = (long)units * (S + 1) * 128 / 4;
-  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream, w, quads);
+  CQ_LAUNCH(qf_init, dim3((unsigned)((quads + 255) / 256)), dim3(256), 0, a.stream, w, quads, a.reset_status);
   const __half* x = (const __half*)a.x;
   int n = a.n, Sv = S, un = units;
   void* args[] = {(void*)&x, (void*)&n, (void*)&un, (void*)&Sv, (void*)&a.codes, (void*)&a.scale,

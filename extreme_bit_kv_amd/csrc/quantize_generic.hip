@@ -61,7 +61,8 @@ __device__ __forceinline__ void load_vals(const T* p, float (&v)[N]) {
 // (channels kVec cg .. +kVec-1), kRows rows of the chunk at a time.
 template <typename T>
 __global__ void __launch_bounds__(kThreads) qz_stats(const T* __restrict__ x, int n, int chunks,
-                                                     float2* __restrict__ part) {
+                                                     float2* __restrict__ part, int* status) {
+  if (status != nullptr && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) *status = 0;
   constexpr int kVec = 16 / (int)sizeof(T), kTpr = kD / kVec, kRows = kThreads / kTpr;
   const int unit = blockIdx.y, chunk = blockIdx.x;
   const T* xu = x + (size_t)unit * n * kD;
@@ -270,8 +271,9 @@ __global__ void __launch_bounds__(kThreads) qz_pack_v(const T* __restrict__ x, R
 }
 
 // Empty cache: scale = minv = 0.
-__global__ void qz_zero(float* scale, float* minv, long count) {
+__global__ void qz_zero(float* scale, float* minv, long count, int* status) {
   long i = (long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (status != nullptr && i == 0) *status = 0;
   if (i < count) {
     scale[i] = 0.0f;
     minv[i] = 0.0f;
@@ -313,14 +315,15 @@ hipError_t run(const cqi::QuantArgs& a) {
   if (a.n == 0) {
     long cnt = (long)units * a.d;
     CQ_LAUNCH(qz_zero, dim3((unsigned)((cnt + 255) / 256)), dim3(256), 0, a.stream,
-                       a.scale, a.minv, cnt);
+                       a.scale, a.minv, cnt, a.reset_status && a.ws != nullptr ? (int*)a.ws : nullptr);
     return hipSuccess;
   }
   const int chunks = (a.n + kChunk - 1) / kChunk;
-  float2* part = (float2*)a.ws;
-  QParams* prm = (QParams*)((char*)a.ws + cqi::align_up((size_t)units * chunks * a.d * sizeof(float2), 256));
+  int* status = a.reset_status ? (int*)a.ws : nullptr;       // this path never waits: status 0
+  float2* part = (float2*)((char*)a.ws + cqi::kWsHeader);
+  QParams* prm = (QParams*)((char*)part + cqi::align_up((size_t)units * chunks * a.d * sizeof(float2), 256));
   const T* x = (const T*)a.x;
-  CQ_LAUNCH(qz_stats<T>, dim3(chunks, units), dim3(kThreads), 0, a.stream, x, a.n, chunks, part);
+  CQ_LAUNCH(qz_stats<T>, dim3(chunks, units), dim3(kThreads), 0, a.stream, x, a.n, chunks, part, status);
   CQ_LAUNCH(qz_params, dim3(units), dim3(a.d), 0, a.stream, part, chunks, a.d, a.bits, a.scale, a.minv,
                      prm);
   const Rows g{(long)a.n, 0, a.n, a.n};
@@ -335,7 +338,7 @@ namespace cqi {
 size_t quant_generic_ws(int B, int H, int n, int d) {
   const size_t units = (size_t)B * H;
   const size_t chunks = (size_t)(n + kChunk - 1) / kChunk;
-  return align_up(units * chunks * d * sizeof(float2), 256) + align_up(units * d * sizeof(QParams), 256);
+  return kWsHeader + align_up(units * chunks * d * sizeof(float2), 256) + align_up(units * d * sizeof(QParams), 256);
 }
 
 hipError_t quant_generic(const QuantArgs& a) {

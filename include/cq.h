@@ -57,14 +57,16 @@
 extern "C" {
 #endif
 
-#define CQ_ABI_VERSION 1
+#define CQ_ABI_VERSION 2
 
 typedef enum {
   CQ_OK = 0,
   CQ_ERR_INVALID_ARG = 1,   /* NULL pointer, negative or inconsistent size, bad enum */
   CQ_ERR_UNSUPPORTED = 2,   /* valid arguments this build does not implement (e.g. d != 128) */
   CQ_ERR_WORKSPACE = 3,     /* workspace pointer NULL or smaller than the query returned */
-  CQ_ERR_HIP = 4            /* a HIP runtime call failed */
+  CQ_ERR_HIP = 4,           /* a HIP runtime call failed */
+  CQ_ERR_TIMEOUT = 5        /* cq_quantize_status: a workgroup of the last quantize call on the
+                               workspace gave up waiting; that call's outputs are invalid */
 } cq_status;
 
 typedef enum { CQ_F16 = 0, CQ_F32 = 1 } cq_dtype;
@@ -111,9 +113,15 @@ typedef struct {
                        value > 0 selects the generic decode.  CQ_PATH_FAST_SPLIT:
                        chunks per (batch, kv head), 0 = automatic, rounded so that
                        a chunk is 4, 8, 16 or 32 tiles of 128 tokens. */
+  int32_t max_polls; /* quantization: unsuccessful polls of a rendezvous word after
+                       which a workgroup of the fused path gives up (and the call's
+                       status word reads 1); 0 = the default bound of a few seconds,
+                       negative -> CQ_ERR_INVALID_ARG.  A small value forces the
+                       time-out path from the host (tests). */
 } cq_opts;
 
-/* ABI version of the loaded library (CQ_ABI_VERSION). */
+/* ABI version of the loaded library (CQ_ABI_VERSION).  Version 2 added
+ * cq_opts.max_polls, CQ_ERR_TIMEOUT and cq_quantize_status. */
 int32_t cq_abi_version(void);
 
 /* hipError_t of the most recent CQ_ERR_HIP returned on the calling thread
@@ -137,12 +145,17 @@ const char* cq_status_str(cq_status s);
  *   scale     device, float32 [B][H][d]: (max - min)/L, correctly rounded
  *   minv      device, float32 [B][H][d]: per-channel minimum (exact)
  *   workspace device, >= cq_quantize_kv_workspace(...) bytes (may be NULL
- *             when that is 0).  After the call completes, its first int32 is
- *             a status word: 0, or 1 if a workgroup of the fused path gave up
+ *             when that is 0).  Its first 256 bytes are a header on every
+ *             path; the first int32 is a status word that the call sets to 0
+ *             and that a workgroup of the fused path sets to 1 if it gave up
  *             waiting for the other chunks of its (batch, head) (the outputs
- *             are then invalid).  The fused path launches no more workgroups
- *             than the device holds at once; a time-out needs other work to
- *             keep part of the device busy for seconds.  CQ_PATH_GENERIC has
+ *             are then invalid).  cq_quantize_status reads it.  The second
+ *             int32 is set to 1 by every call that timed out and is never
+ *             cleared by the library: a caller that zeroes it once can check
+ *             a whole run of calls at its end.  The fused
+ *             path launches no more workgroups than the device holds at once;
+ *             a time-out needs other work to keep part of the device busy
+ *             for seconds (or a small opts->max_polls).  CQ_PATH_GENERIC has
  *             no such wait.
  *   The fused path takes fp16 input at b = 1 when every 512-token chunk of a
  *   (b, h) fits on the device at once (n <= 512 x the co-resident workgroups,
@@ -181,6 +194,24 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype,
  * Errors and limits as for cq_quantize_kv.
  * ------------------------------------------------------------------------ */
 size_t cq_quantize_kv_pair_workspace(int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits);
+
+/* ------------------------------------------------------------------------
+ * cq_quantize_status — whether the last cq_quantize_kv / cq_quantize_kv_pair
+ * call on `workspace` completed every wait of its fused kernel ([ART] Method
+ * part 1 takes each channel's range over all n tokens of a head, so the
+ * chunks of one head meet before any code is decided).
+ *
+ *   workspace  device, the workspace that call used (>= 4 bytes, 16-byte
+ *              aligned)
+ *   stream     the stream that call was enqueued on; it is synchronized
+ *              (the status word is read after all earlier work on it)
+ * Returns CQ_OK when no workgroup gave up, CQ_ERR_TIMEOUT when one did (the
+ * call's codes, scales and minima are then invalid), CQ_ERR_INVALID_ARG for
+ * a NULL or misaligned workspace, CQ_ERR_HIP if the copy or the
+ * synchronization failed.  Enqueues a 4-byte device-to-host copy; allocates
+ * nothing.
+ * ------------------------------------------------------------------------ */
+cq_status cq_quantize_status(const void* workspace, void* stream);
 
 cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype,
                               int32_t B, int32_t H, int32_t n, int32_t d, int32_t bits,

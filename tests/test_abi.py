@@ -29,9 +29,10 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_status_strings():
-    assert lib.cq_abi_version() == 1
-    for s in range(5):
+    assert lib.cq_abi_version() == 2
+    for s in range(6):
         assert lib.cq_status_str(s)
+    assert b"TIMEOUT" in lib.cq_status_str(5)
     assert b"unknown" in lib.cq_status_str(99)
 
 
@@ -209,6 +210,7 @@ def _pair(**kw):
     (dict(k=None), 1), (dict(v=None), 1), (dict(kc=None), 1), (dict(vc=None), 1), (dict(ks=None), 1),
     (dict(vm=None), 1), (dict(bits=3), 1), (dict(dt=7), 1), (dict(n=-1), 1), (dict(d=48), 1), (dict(d=64), 2),
     (dict(opts=ctypes.pointer(cqb.cq_opts(9, 0))), 1), (dict(v=ODD), 1), (dict(vc=ODD), 1), (dict(ws=ODD), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(0, 0, -1))), 1),                # negative poll limit
 ])
 def test_quantize_pair_rejects(kw, status):
     assert _pair(**kw) == status
@@ -218,3 +220,13 @@ def test_quantize_pair_workspace_query():
     assert lib.cq_quantize_kv_pair_workspace(64, 8, 8192, 128, 1) >= lib.cq_quantize_kv_workspace(64, 8, 8192, 128, 1)
     assert lib.cq_quantize_kv_pair_workspace(1, 1, 256, 128, 3) == 0
     assert _pair(B=0, k=None, v=None, kc=None, ks=None, km=None, vc=None, vs=None, vm=None, ws=None, wsb=0) == 0
+
+
+def test_quantize_status_rejects_before_any_copy():
+    """cq_quantize_status validates its workspace pointer before touching the GPU."""
+    assert lib.cq_quantize_status(None, None) == 1
+    assert lib.cq_quantize_status(ODD, None) == 1
+
+
+def test_quantize_rejects_negative_poll_limit():
+    assert _quant(opts=ctypes.pointer(cqb.cq_opts(0, 0, -5))) == 1

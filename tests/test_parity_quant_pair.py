@@ -102,3 +102,47 @@ def test_pair_several_rounds_ragged(B, H, n):
             c, sc, mn, _ = oracle.quantize_unit(x[b, h].cpu().numpy(), 1)
             assert np.array_equal(words_u32(words[b, h]), oracle.pack(c, 1, layout))
             assert np.array_equal(scale[b, h].cpu().numpy().view(np.uint32), sc.view(np.uint32))
+
+
+@pytest.mark.parametrize("pair", [True, False])
+def test_wait_time_out_is_reported(pair):
+    """A fused call whose workgroups give up waiting (forced from the host
+    with cq_opts.max_polls = 1: every kernel still exits normally) raises
+    CQ_ERR_TIMEOUT through cq_quantize_status, and the header word that
+    collects time-outs keeps the record; the next call with the default
+    bound clears the call's status word and is exact again."""
+    import torch
+    B, H, n = 16, 8, 8192                        # 16 chunks per (batch, head): every head has waits
+    K, V, *_ = draw_inputs(B, 4 * H, H, n, 0, seed=91, host=False)
+    size = (cqb.lib.cq_quantize_kv_pair_workspace if pair else cqb.lib.cq_quantize_kv_workspace)(B, H, n, 128, 1)
+    ws = torch.zeros(size, dtype=torch.uint8, device="cuda")
+
+    def call(**kw):
+        if pair:
+            return cqb.cq_quantize_kv_pair(K, V, 1, workspace=ws, **kw)[0]
+        return cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K, workspace=ws, **kw)
+
+    note(f"quantize forced time-out pair={pair}")
+    with pytest.raises(cqb.CQError) as ei:
+        call(check=True, max_polls=1)
+    assert ei.value.status == cqb.CQ_ERR_TIMEOUT
+    assert int(ws[4:8].view(torch.int32).item()) == 1
+    note(f"quantize after a time-out pair={pair}")
+    kc, ks, km = call(check=True)                # raises if any wait gave up
+    assert int(ws[:4].view(torch.int32).item()) == 0
+    assert int(ws[4:8].view(torch.int32).item()) == 1      # the collected record stays
+    kw, kso, kmo, _ = oracle.quantize(K[5:6, 3:4].cpu().numpy(), 1, "K")
+    assert np.array_equal(words_u32(kc[5:6, 3:4]), kw)
+    assert np.array_equal(ks[5:6, 3:4].cpu().numpy(), kso) and np.array_equal(km[5:6, 3:4].cpu().numpy(), kmo)
+
+
+def test_generic_path_reports_no_time_out():
+    """Float32 input runs K and V one after the other through the generic
+    kernels on one workspace (the fused launch takes float16 only).  They
+    never wait, so the status words stay 0 whatever the poll limit."""
+    import torch
+    K, V, *_ = draw_inputs(2, 8, 2, 1024, 0, dtype="float32", seed=92, host=False)
+    ws = torch.zeros(cqb.lib.cq_quantize_kv_pair_workspace(2, 2, 1024, 128, 1), dtype=torch.uint8, device="cuda")
+    note("quantize pair fp32 with a poll limit")
+    cqb.cq_quantize_kv_pair(K, V, 1, workspace=ws, check=True, max_polls=1)
+    assert int(ws[4:8].view(torch.int32).item()) == 0
