@@ -29,7 +29,8 @@ lib = ctypes.CDLL(LIB_PATH)
 CQ_OK, CQ_ERR_INVALID_ARG, CQ_ERR_UNSUPPORTED, CQ_ERR_WORKSPACE, CQ_ERR_HIP, CQ_ERR_TIMEOUT = range(6)
 CQ_F16, CQ_F32 = 0, 1
 CQ_LAYOUT_K, CQ_LAYOUT_V = 0, 1
-CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT, CQ_PATH_FAST_LDS = 0, 1, 2, 3, 4, 5
+CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT, CQ_PATH_FAST_LDS, CQ_PATH_FAST_PIPE = (
+    0, 1, 2, 3, 4, 5, 6)
 
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",

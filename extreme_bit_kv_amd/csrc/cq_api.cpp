@@ -77,7 +77,7 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
     return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (scale == nullptr || minv == nullptr) return CQ_ERR_INVALID_ARG;
@@ -111,7 +111,7 @@ cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, in
   if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype)) return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (k_scale == nullptr || k_min == nullptr || v_scale == nullptr || v_min == nullptr) return CQ_ERR_INVALID_ARG;
@@ -222,7 +222,7 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
   if ((d * bits) % 32 != 0 || n + (int64_t)T < 1) return CQ_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale)) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_LDS || (opts && opts->splits < 0)) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || (opts && opts->splits < 0)) return CQ_ERR_INVALID_ARG;
   if (B > 0) {
     if (q == nullptr || out == nullptr) return CQ_ERR_INVALID_ARG;
     if (n > 0 && (k_codes == nullptr || k_scale == nullptr || k_min == nullptr || v_codes == nullptr ||
@@ -251,10 +251,14 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
   a.stream = (hipStream_t)stream;
   const bool one_ok = cqi::decode_fast_supported(a);
   const bool split_ok = cqi::decode_split_supported(a);
-  enum { kGeneric, kOne, kSplit, kLds } use = kGeneric;
+  const bool pipe_ok = cqi::decode_pipe_supported(a);
+  enum { kGeneric, kOne, kSplit, kLds, kPipe } use = kGeneric;
   if (path == CQ_PATH_FAST_LDS) {
     if (!cqi::decode_lds_supported(a)) return CQ_ERR_UNSUPPORTED;
     use = kLds;
+  } else if (path == CQ_PATH_FAST_PIPE) {
+    if (!pipe_ok) return CQ_ERR_UNSUPPORTED;
+    use = kPipe;
   } else if (path == CQ_PATH_FAST_ONE) {
     if (!one_ok) return CQ_ERR_UNSUPPORTED;
     use = kOne;
@@ -269,11 +273,13 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
   }
   const int req = use == kSplit && path == CQ_PATH_FAST_SPLIT ? a.splits : 0;
   size_t need;
-  if (use == kOne || use == kLds) need = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
+  if (use == kPipe) need = 0;
+  else if (use == kOne || use == kLds) need = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
   else if (use == kSplit) need = cqi::decode_split_ws(B, Hkv, n, T, req);
   else need = cqi::decode_generic_ws(B, Hq, Hkv, n, T, d, cqi::decode_generic_splits(n, B * Hkv, a.splits));
   if (B > 0 && need > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
   clear_stale_hip_error();
+  if (use == kPipe) return from_hip(cqi::decode_pipe(a));
   if (use == kLds) return from_hip(cqi::decode_lds(a));
   if (use == kOne) return from_hip(cqi::decode_fast(a));
   if (use == kSplit) return from_hip(cqi::decode_split(a, req));

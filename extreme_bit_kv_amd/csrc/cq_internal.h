@@ -89,6 +89,12 @@ int decode_generic_splits(int n, int units, int requested);
 size_t decode_generic_ws(int B, int Hq, int Hkv, int n, int T, int d, int splits);
 hipError_t decode_generic(const DecodeArgs& a);
 
+// b = 1, keys read once with the visual scores kept in registers (one 8-wave
+// workgroup per CU walking its units, the value pass of one unit beside the key
+// pass of the next)
+bool decode_pipe_supported(const DecodeArgs& a);
+hipError_t decode_pipe(const DecodeArgs& a);
+
 // b = 1, visual scores kept in LDS (one 16-wave workgroup per CU walking its units)
 bool decode_lds_supported(const DecodeArgs& a);
 bool decode_lds_preferred(const DecodeArgs& a);   // the automatic choice

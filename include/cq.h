@@ -101,10 +101,19 @@ typedef struct {
  *                       (batch, kv head) units, the visual scores kept in LDS
  *                       between the key and the value pass (the keys are
  *                       read once); results equal CQ_PATH_FAST_ONE's bit for
- *                       bit. */
+ *                       bit.
+ *   CQ_PATH_FAST_PIPE   b = 1 only, G in {1, 2, 4}, 32 <= n <= 8192, n a
+ *                       multiple of 32, T <= 128: one launch of one 8-wave
+ *                       workgroup per CU walking its units, the value pass of
+ *                       one unit run beside the key pass of the next; the
+ *                       keys are read once and the scores stay on chip.  The
+ *                       key dot products take the query as four signed base-31
+ *                       digits (about 20 bits, against 22 on the other fast
+ *                       paths), so its results match CQ_PATH_FAST_ONE's to the
+ *                       2e-3 tolerance, not bit for bit.  Needs no workspace. */
 typedef enum {
   CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4,
-  CQ_PATH_FAST_LDS = 5
+  CQ_PATH_FAST_LDS = 5, CQ_PATH_FAST_PIPE = 6
 } cq_path;
 typedef struct {
   int32_t path;     /* cq_path; a FAST path on an unsupported shape -> CQ_ERR_UNSUPPORTED */

@@ -86,10 +86,16 @@ def _decode(**kw):
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
-    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0))), 1),              # no such path
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0))), 1),              # no such path
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), bits=2), 2),     # LDS-score schedule: b = 1 only ...
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), n=8320), 2),     # ... and G x ceil(n/128) <= 256
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), Hq=24), 2),      # ... and G in 1, 2, 4
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), bits=2), 2),     # pipelined schedule: b = 1 only ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), n=8224), 2),     # ... 32 <= n <= 8192 ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), n=0, kc=None, vc=None), 2),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), T=129), 2),      # ... T <= 128 ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), n=80), 2),       # ... n a multiple of 32
+    (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), Hq=48), 2),      # ... G in 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),      # one-launch schedule: group sizes 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), bits=2), 2),     # split schedule: b = 1 only
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=0, kc=None, vc=None), 2),   # ... and n > 0

@@ -33,7 +33,8 @@ REVERSED_REL = (1.0, 0.0, 0.5, 0.0)    # t_hi = M/2 < t_lo = m on scores in [m, 
 IDENTITY = (1.0, 0.0, 1.0, 0.0)
 
 P = cqb
-B1_PATHS = [P.CQ_PATH_GENERIC, P.CQ_PATH_AUTO, P.CQ_PATH_FAST_ONE, P.CQ_PATH_FAST_LDS, P.CQ_PATH_FAST_SPLIT]
+B1_PATHS = [P.CQ_PATH_GENERIC, P.CQ_PATH_AUTO, P.CQ_PATH_FAST_ONE, P.CQ_PATH_FAST_LDS, P.CQ_PATH_FAST_PIPE,
+            P.CQ_PATH_FAST_SPLIT]
 BN_PATHS = [P.CQ_PATH_GENERIC, P.CQ_PATH_AUTO, P.CQ_PATH_FAST_ONE]
 
 
@@ -133,6 +134,8 @@ def _takes(path, bits, G, n, T):
         return fast and bits == 1 and n > 0
     if path == P.CQ_PATH_FAST_LDS:
         return fast and bits == 1 and G * -(-n // 128) <= 256
+    if path == P.CQ_PATH_FAST_PIPE:
+        return fast and bits == 1 and 32 <= n <= 8192 and T <= 128
     return True
 
 
