@@ -35,7 +35,8 @@ CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLI
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
             "cq_decode_attn_fp16_workspace", "cq_decode_attn_fp16", "cq_scores_fp16", "cq_kv_range_update",
-            "cq_quantize_kv_rows", "cq_quantize_kv_pair_workspace", "cq_quantize_kv_pair", "cq_quantize_status")
+            "cq_quantize_kv_rows", "cq_quantize_kv_pair_workspace", "cq_quantize_kv_pair", "cq_quantize_status",
+            "cq_decode_attn_noalloc")
 
 
 class cq_calib(ctypes.Structure):
@@ -76,6 +77,9 @@ lib.cq_decode_attn.restype = _i32
 lib.cq_decode_attn.argtypes = ([_vp, _i32] + [_vp] * 6 + [_vp, _vp, _i32] + [_i32] * 7 +
                                [_f32, ctypes.POINTER(cq_calib), _vp, _i32, _vp, _sz,
                                 ctypes.POINTER(cq_opts), _vp])
+lib.cq_decode_attn_noalloc.restype = _i32
+lib.cq_decode_attn_noalloc.argtypes = ([_vp, _i32] + [_vp] * 6 + [_vp, _vp, _i32] + [_i32] * 7 +
+                                       [_f32, ctypes.POINTER(cq_calib), _vp, _i32, ctypes.POINTER(cq_opts), _vp])
 lib.cq_visual_scores.restype = _i32
 lib.cq_visual_scores.argtypes = [_vp, _i32, _vp, _vp, _vp] + [_i32] * 6 + [_f32, _vp, _vp]
 lib.cq_scores_fp16.restype = _i32
@@ -188,10 +192,9 @@ def cq_quantize_kv(x, bits: int, layout: int, codes=None, scale=None, minv=None,
     return codes, scale, minv
 
 
-def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, *, n: int,
-                   bits: int, sm_scale: float, calib=None, out=None, out_dtype=None, workspace=None,
-                   path: int = CQ_PATH_AUTO, splits: int = 0):
-    """One decode step; q [B, Hq, d]; codes/params from cq_quantize_kv; tails [B, Hkv, T, d] or None."""
+def _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, n, bits, out,
+                    out_dtype):
+    """Checks of the decode operands; returns (B, Hq, Hkv, T, d, tail dtype code, out, leading C args)."""
     torch = _torch()
     _need(q, "q")
     B, Hq, d = q.shape
@@ -211,19 +214,43 @@ def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, 
     if out is None:
         out = torch.empty((B, Hq, d), dtype=out_dtype or q.dtype, device=dev)
     _need(out, "out", (B, Hq, d), None, dev)
+    lead = (_ptr(q), _dtype_code(q), _ptr(k_codes) if n else None, _ptr(k_scale), _ptr(k_min),
+            _ptr(v_codes) if n else None, _ptr(v_scale), _ptr(v_min), _ptr(k_tail) if T else None,
+            _ptr(v_tail) if T else None, tail_code, B, Hq, Hkv, n, T, d, bits)
+    return B, Hq, Hkv, T, d, out, lead
+
+
+def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, *, n: int,
+                   bits: int, sm_scale: float, calib=None, out=None, out_dtype=None, workspace=None,
+                   path: int = CQ_PATH_AUTO, splits: int = 0):
+    """One decode step; q [B, Hq, d]; codes/params from cq_quantize_kv; tails [B, Hkv, T, d] or None."""
+    torch = _torch()
+    B, Hq, Hkv, T, d, out, lead = _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
+                                                  v_tail, n, bits, out, out_dtype)
     ws_bytes = lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, bits)
     if workspace is None and ws_bytes:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     c = make_calib(calib)
     opts = cq_opts(path, splits, 0)
-    st = lib.cq_decode_attn(_ptr(q), _dtype_code(q), _ptr(k_codes) if n else None, _ptr(k_scale),
-                            _ptr(k_min), _ptr(v_codes) if n else None, _ptr(v_scale), _ptr(v_min),
-                            _ptr(k_tail) if T else None, _ptr(v_tail) if T else None, tail_code,
-                            B, Hq, Hkv, n, T, d, bits, float(sm_scale),
-                            None if c is None else ctypes.byref(c), _ptr(out), _dtype_code(out),
-                            _ptr(workspace), 0 if workspace is None else workspace.numel(),
-                            ctypes.byref(opts), _stream(dev))
+    st = lib.cq_decode_attn(*lead, float(sm_scale), None if c is None else ctypes.byref(c), _ptr(out),
+                            _dtype_code(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
+                            ctypes.byref(opts), _stream(q.device))
     _check(st, "cq_decode_attn")
+    return out
+
+
+def cq_decode_attn_noalloc(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, *, n: int,
+                           bits: int, sm_scale: float, out, calib=None, path: int = CQ_PATH_AUTO,
+                           splits: int = 0):
+    """cq_decode_attn into a caller's `out` with the library's fixed device
+    scratch: no device memory is allocated, here or in the library."""
+    _, _, _, _, _, out, lead = _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
+                                               v_tail, n, bits, out, None)
+    c = make_calib(calib)
+    opts = cq_opts(path, splits, 0)
+    st = lib.cq_decode_attn_noalloc(*lead, float(sm_scale), None if c is None else ctypes.byref(c), _ptr(out),
+                                    _dtype_code(out), ctypes.byref(opts), _stream(q.device))
+    _check(st, "cq_decode_attn_noalloc")
     return out
 
 

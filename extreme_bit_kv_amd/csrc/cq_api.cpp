@@ -210,12 +210,18 @@ size_t cq_decode_attn_workspace(int32_t B, int32_t Hq, int32_t Hkv, int32_t n, i
   return m > c ? m : c;
 }
 
-cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
-                         const float* k_min, const uint32_t* v_codes, const float* v_scale, const float* v_min,
-                         const void* k_tail, const void* v_tail, cq_dtype tail_dtype, int32_t B, int32_t Hq,
-                         int32_t Hkv, int32_t n, int32_t T, int32_t d, int32_t bits, float sm_scale,
-                         const cq_calib* calib, void* out, cq_dtype out_dtype, void* workspace,
-                         size_t workspace_bytes, const cq_opts* opts, void* stream) {
+static_assert(CQ_NOALLOC_SCRATCH_BYTES == cqi::kScratchBytes, "scratch size of the header and the library");
+
+namespace {
+
+// cq_decode_attn and cq_decode_attn_noalloc; with `fixed_scratch` the
+// workspace is the device's fixed scratch array (the caller's pointer is NULL).
+cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
+                       const float* k_min, const uint32_t* v_codes, const float* v_scale, const float* v_min,
+                       const void* k_tail, const void* v_tail, cq_dtype tail_dtype, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t n, int32_t T, int32_t d, int32_t bits, float sm_scale,
+                       const cq_calib* calib, void* out, cq_dtype out_dtype, void* workspace,
+                       size_t workspace_bytes, bool fixed_scratch, const cq_opts* opts, void* stream) {
   if (!fits(B, Hq, n, d) || !fits(B, Hkv, T, d) || Hkv <= 0 || Hq <= 0 || Hq % Hkv != 0 || d <= 0 ||
       !valid_bits(bits) || !valid_dtype(q_dtype) || !valid_dtype(out_dtype) || !valid_dtype(tail_dtype))
     return CQ_ERR_INVALID_ARG;
@@ -277,13 +283,47 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_code
   else if (use == kOne || use == kLds) need = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
   else if (use == kSplit) need = cqi::decode_split_ws(B, Hkv, n, T, req);
   else need = cqi::decode_generic_ws(B, Hq, Hkv, n, T, d, cqi::decode_generic_splits(n, B * Hkv, a.splits));
-  if (B > 0 && need > 0 && (workspace == nullptr || workspace_bytes < need)) return CQ_ERR_WORKSPACE;
+  if (fixed_scratch) {
+    if (need > cqi::kScratchBytes) return CQ_ERR_WORKSPACE;
+    if (B > 0) {
+      clear_stale_hip_error();
+      void* ptr = nullptr;
+      const hipError_t e = cqi::scratch_address(&ptr);
+      if (e != hipSuccess) return from_hip(e);
+      a.ws = ptr;
+    }
+  } else if (B > 0 && need > 0 && (workspace == nullptr || workspace_bytes < need)) {
+    return CQ_ERR_WORKSPACE;
+  }
   clear_stale_hip_error();
   if (use == kPipe) return from_hip(cqi::decode_pipe(a));
   if (use == kLds) return from_hip(cqi::decode_lds(a));
   if (use == kOne) return from_hip(cqi::decode_fast(a));
   if (use == kSplit) return from_hip(cqi::decode_split(a, req));
   return from_hip(cqi::decode_generic(a));
+}
+
+}  // namespace
+
+cq_status cq_decode_attn(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
+                         const float* k_min, const uint32_t* v_codes, const float* v_scale, const float* v_min,
+                         const void* k_tail, const void* v_tail, cq_dtype tail_dtype, int32_t B, int32_t Hq,
+                         int32_t Hkv, int32_t n, int32_t T, int32_t d, int32_t bits, float sm_scale,
+                         const cq_calib* calib, void* out, cq_dtype out_dtype, void* workspace,
+                         size_t workspace_bytes, const cq_opts* opts, void* stream) {
+  return decode_entry(q, q_dtype, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, tail_dtype, B,
+                      Hq, Hkv, n, T, d, bits, sm_scale, calib, out, out_dtype, workspace, workspace_bytes, false,
+                      opts, stream);
+}
+
+cq_status cq_decode_attn_noalloc(const void* q, cq_dtype q_dtype, const uint32_t* k_codes, const float* k_scale,
+                                 const float* k_min, const uint32_t* v_codes, const float* v_scale,
+                                 const float* v_min, const void* k_tail, const void* v_tail, cq_dtype tail_dtype,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t T, int32_t d, int32_t bits,
+                                 float sm_scale, const cq_calib* calib, void* out, cq_dtype out_dtype,
+                                 const cq_opts* opts, void* stream) {
+  return decode_entry(q, q_dtype, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, tail_dtype, B,
+                      Hq, Hkv, n, T, d, bits, sm_scale, calib, out, out_dtype, nullptr, 0, true, opts, stream);
 }
 
 // ---------------------------------------------------------------------------

@@ -95,6 +95,11 @@ hipError_t decode_generic(const DecodeArgs& a);
 bool decode_pipe_supported(const DecodeArgs& a);
 hipError_t decode_pipe(const DecodeArgs& a);
 
+// Per-device fixed scratch of the entry points that allocate nothing: its
+// device address on the current device (resolved once per device).
+constexpr size_t kScratchBytes = (size_t)16 << 20;
+hipError_t scratch_address(void** out);
+
 // b = 1, visual scores kept in LDS (one 16-wave workgroup per CU walking its units)
 bool decode_lds_supported(const DecodeArgs& a);
 bool decode_lds_preferred(const DecodeArgs& a);   // the automatic choice

@@ -342,6 +342,35 @@ cq_status cq_decode_attn(const void* q, cq_dtype q_dtype,
                          const cq_opts* opts, void* stream);
 
 /* ------------------------------------------------------------------------
+ * cq_decode_attn_noalloc — cq_decode_attn for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments and results as
+ * cq_decode_attn with the same opts, minus the workspace: the schedules that
+ * need one use a fixed scratch array of CQ_NOALLOC_SCRATCH_BYTES that the
+ * library holds on every device it runs on until the process ends.  The
+ * call allocates nothing (no hipMalloc, no hipFree); its first call on a
+ * device resolves that device's scratch address (the current device must be
+ * the stream's).  Calls that need more scratch than the array holds return
+ * CQ_ERR_WORKSPACE before enqueuing anything (cq_decode_attn with a
+ * workspace takes them).  Every call on a device shares its one array, and
+ * the array keeps the last call's contents (no schedule reads scratch it has
+ * not written in the same call): calls on one device whose executions
+ * overlap (different streams, or different host threads) race and give
+ * wrong results; calls in order on one stream are safe.
+ * ------------------------------------------------------------------------ */
+#define CQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+
+cq_status cq_decode_attn_noalloc(const void* q, cq_dtype q_dtype,
+                                 const uint32_t* k_codes, const float* k_scale, const float* k_min,
+                                 const uint32_t* v_codes, const float* v_scale, const float* v_min,
+                                 const void* k_tail, const void* v_tail, cq_dtype tail_dtype,
+                                 int32_t B, int32_t Hq, int32_t Hkv, int32_t n, int32_t T,
+                                 int32_t d, int32_t bits, float sm_scale,
+                                 const cq_calib* calib,
+                                 void* out, cq_dtype out_dtype,
+                                 const cq_opts* opts, void* stream);
+
+/* ------------------------------------------------------------------------
  * cq_visual_scores — the pre-softmax visual scores of cq_decode_attn on their
  * own, for inspection and diagnostics ([ART] Method part 2; before g):
  *   scores[b][hq][i] = sm_scale*(q*k_scale).c_i + sm_scale*q.k_min,

@@ -107,6 +107,34 @@ def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
 
 
+def _decode_noalloc(**kw):
+    a = dict(q=FAKE, qdt=0, kc=FAKE, ks=FAKE, km=FAKE, vc=FAKE, vs=FAKE, vm=FAKE, kt=FAKE, vt=FAKE, tdt=0,
+             B=2, Hq=32, Hkv=8, n=64, T=8, d=128, bits=1, sm=0.088, calib=None, out=FAKE, odt=0, opts=None)
+    a.update(kw)
+    return lib.cq_decode_attn_noalloc(a["q"], a["qdt"], a["kc"], a["ks"], a["km"], a["vc"], a["vs"], a["vm"],
+                                      a["kt"], a["vt"], a["tdt"], a["B"], a["Hq"], a["Hkv"], a["n"], a["T"],
+                                      a["d"], a["bits"], a["sm"], a["calib"], a["out"], a["odt"], a["opts"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), 1), (dict(out=None), 1), (dict(kc=None), 1), (dict(T=0), 1), (dict(Hq=30), 1),
+    (dict(bits=5), 1), (dict(d=64), 2), (dict(kc=ODD), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0))), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),
+    # the generic schedule's scores of 64 x 32 heads x 8192 tokens take 64 MiB:
+    # beyond the fixed scratch, refused before anything is enqueued
+    (dict(opts=ctypes.pointer(cqb.cq_opts(1, 0)), B=64, n=8192, T=0, kt=None, vt=None), 3),
+    (dict(B=0, q=None, out=None, kc=None, ks=None, km=None, vc=None, vs=None, vm=None, kt=None, vt=None), 0),
+])
+def test_decode_noalloc_rejects(kw, status):
+    assert _decode_noalloc(**kw) == status
+
+
+def test_noalloc_scratch_size_is_declared():
+    text = open(os.path.join(ROOT, "include", "cq.h")).read()
+    assert "#define CQ_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)" in text
+
+
 def test_calibrate_rejects():
     c = cqb.cq_calib(1, 0.9, 0.0, 0.8, 0.0)
     assert lib.cq_calibrate(FAKE, 4, 0, ctypes.byref(c), FAKE, None, None) == 1
