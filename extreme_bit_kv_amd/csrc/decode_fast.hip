@@ -12,21 +12,26 @@
 // does not hold the others at the next barrier.  Two workgroups fit on a CU,
 // so a whole decode step (every unit of the batch) is resident at once.
 //
-// K side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16] with
-// v_mfma_i32_16x16x64_i8, twice (128 channels).  B bytes are code bits left
-// in place in the packed word, one AND per register (bits_lo / bits_hi):
-// channel j's bit sits in its byte with weight 2^s(j), s(j) =
-// min(floor((j mod 32) / 4), 6).  Rows of A are (head, digit plane): each
-// head's q * scale_K is a 22-bit fixed-point integer Q (q' 2^F, rounded),
-// multiplied by 2^(7 - s(j)) for channel j and split into four signed
-// base-256 digits, so every product is 2^7 Q_j c_j and the int32 plane sums
-// are exact.  Columns are tokens.  Each lane ends up holding all planes of
-// one (head, token) score: s = ((a0 + 2^8 a1) + 2^16 (a2 + 2^8 a3)) 2^-(F+7)
-// + c0, the two halves exact in int32 and their sum rounded to float the same
-// way in both passes.  The first pass over the keys only gathers every
-// head's min and max, which fix g; the value pass reads the key tiles again
-// (they are still in the Infinity Cache) and recomputes the same scores,
-// instead of keeping 4 B per head and token on chip.
+// K side, per tile (b = 1): C[16 x 16] = A[16 x 128] B[128 x 16] with the
+// 16x16x128 f8f6f4 product, A in fp6 (e2m3), B in fp4 (e2m1).  B is the
+// packed key word masked in place, one operation per register: the fields
+// whose code sits in bit 0, 1 or 2 read 0.5 c, c or 2 c, the bit-3 fields
+// are forced to +-1 (1 - 2 c).  Rows of A are (head, digit plane): each
+// head's q * scale_K is the integer Q = round(q' 2^F) (|Q| below 2^18.8, F
+// from the largest |q'|) in four balanced base-31 digits d in [-15, 15],
+// each stored as d / 2, d / 4, d / 8 or -d / 8 for the four field kinds, so
+// every product is exactly d c / 4, every plane sum is exact in float32, and
+// the bit-3 fields leave the constant -Q / 8 per channel, added back to the
+// head's offset with q . min_K.  Columns are tokens; each lane ends up with
+// all four planes of one (head, token) score s = ((D0 31 + D1) 31 + D2) 31 +
+// D3, formed by the same operations in both passes and kept in these units
+// (the statistics take the scale 4 2^-F and the offset).  The first pass
+// over the keys only gathers every head's min and max, which fix g; the
+// value pass reads the key tiles again (they are still in the Infinity
+// Cache) and recomputes the same scores, instead of keeping 4 B per head and
+// token on chip.  Tiles are read with buffer loads: one descriptor per unit
+// and tensor, a fixed byte offset per lane, and a tile past the last reads
+// out of range (zeros, no traffic).
 //
 // V side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16], rows again
 // (head, plane), columns channels, contraction over tokens; B is the masked
@@ -76,6 +81,40 @@ using cqm::lds_barrier;
 // selected once, and the clamped offsets of an empty tensor stay below 512 B.
 __device__ __align__(16) uint32_t g_pad[128];
 
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+constexpr int kQMax = 15 * (31 * 31 * 31 + 31 * 31 + 31 + 1);   // largest |Q| with four base-31 digits
+constexpr int kRsrcFlags = 0x00020000;                            // raw buffer, 32-bit data format
+
+// fp6 e2m3 code of x / 8 for an integer |x| <= 60 that the format holds
+// (|x| < 16, even |x| < 32, or a multiple of 4)
+__device__ __forceinline__ uint32_t enc6(int x) {
+  const uint32_t a = (uint32_t)(x < 0 ? -x : x);
+  uint32_t m;
+  if (a < 16) m = a;
+  else if (a < 32) m = 16 + ((a - 16) >> 1);
+  else m = 24 + ((a - 32) >> 2);
+  return m | (x < 0 ? 0x20u : 0u);
+}
+
+// min / max of three floats in one instruction (never NaN here, so no quieting)
+__device__ __forceinline__ float min3f(float a, float b, float c) {
+  float r;
+  asm("v_min3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+__device__ __forceinline__ float max3f(float a, float b, float c) {
+  float r;
+  asm("v_max3_f32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "v"(c));
+  return r;
+}
+
+__device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
+  return make_uint4(x.x, x.y, x.z, x.w);
+}
+
 struct Params {
   const void* q;
   const uint32_t* kc;
@@ -113,9 +152,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ float s_q[4][128];                 // sm * q, float
   __shared__ float s_qp[4][128];                // sm * q * scale_K
   __shared__ double s_c0[4];
-  __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
-  __shared__ __align__(16) uint32_t s_adig[4][4][32];   // K-side A digits: [head][plane][128 channel bytes]
+  __shared__ __align__(16) uint32_t s_adig[4][4][32];   // K-side fp6 digit codes: [head][plane][128 k slots]
+  __shared__ float s_kc[4];                              // per head: sum of Q / 8 over the bit-3 channels
   __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // V-side A digits: [head][plane][128 token bytes]
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
@@ -146,11 +185,16 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const size_t prm = n > 0 ? (size_t)unit * 128 + pj : (size_t)pj;
   const float q_in = ld_any(P.q, ((size_t)b * P.Hq + h * G + min(ph, G - 1)) * 128 + pj, F32);
   const float ks_in = ksb[prm], km_in = kmb[prm], vs_in = vsb[prm], vm_in = vmb[prm];
+  // Code tiles are read with buffer loads: one descriptor per unit and tensor,
+  // a fixed byte offset per lane plus the tile's (wave-uniform); a tile past
+  // the last reads out of range, which returns zeros without any traffic.
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (n > 0 ? (size_t)unit * 4 * n : 0)), (short)0,
+                                                    n * 16, kRsrcFlags);
+  const uint32_t koff = (uint32_t)(g4 * n + 8 * i16) * 4u;
   auto load_k = [&](int tile, uint4& w0, uint4& w1) {   // tokens past n: scores not used
-    const int tok = max(min(tile * kTile + 8 * i16, n - 8), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)unit * 4 + g4) * n + tok);
-    w0 = src[0];
-    w1 = src[1];
+    const uint32_t off = koff + (tile < ntiles ? (uint32_t)tile * 512u : 0x80000000u);
+    w0 = ld_buf(rk, off);
+    w1 = ld_buf(rk, off + 16u);
   };
   // The first kPreTail tail keys, as (token 4 wave + lane/16 + 32 r, channels
   // 8 (lane%16) ..+7), are requested first: their scores are formed right
@@ -186,7 +230,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     s_next[0] = 2 * kWaves;
     s_next[1] = kWaves;
   }
-  if (tid < 4) s_psum[tid] = 0.0;
+  if (tid < 4) {
+    s_psum[tid] = 0.0;
+    s_kc[tid] = 0.f;
+  }
   for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
   // ---- prologue: post-scaled query, fixed-point digits -------------------
@@ -223,22 +270,40 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
     const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
     int F = 0;
-    if (mq > 0.f) F = 21 - ilogbf(mq);
+    if (mq > 0.f) {
+      const int e = ilogbf(mq);
+      F = ldexpf(mq, 18 - e) > (float)kQMax ? 17 - e : 18 - e;
+    }
     s_F[tid] = F;
-    s_inv2f[tid] = ldexpf(1.f, -F - 3);         // products carry 2^3 (bits_lo / bits_hi)
     s_c0[tid] = c0;
   }
   lds_barrier();
   {
-    // channel j's factor 2^bit_weight(j mod 32) makes up for the place its
-    // code bit keeps in the masked word; the digits are the bytes of
-    // Qs + 0x808080 with the low three offset back by 128 (signed base-256)
+    // Q = round(q' 2^F) in four balanced base-31 digits.  Channel j sits in k
+    // slot 32 (j / 32) + 8 R + 2 (e mod 4) + e / 16 of its row, e = j mod 32,
+    // R = (e / 4) mod 4, the fp4 field of its key bit; its digit is stored as
+    // d / 2, d / 4, d / 8 or -d / 8 (the bit-3 fields read +-1: 1 - 2 c), so
+    // that every product is d c / 4 and the bit-3 channels leave a constant
+    // sum of -Q / 8, added back to the head's offset.
     const int hh = tid >> 7, j = tid & 127;
-    const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));        // |Q| <= 2^22
-    const uint32_t dig = cqm::sdigits((uint32_t)(Q * (1 << bit_weight(j & 31))));   // |Q 2^wt| <= 2^25
+    const float x = rintf(ldexpf(s_qp[hh][j], s_F[hh]));            // |x| <= kQMax, exact
+    float d[4], r = x;
+#pragma unroll
+    for (int k = 3; k > 0; --k) {
+      const float qk = rintf(r * (1.f / 31.f));                      // exact: r / 31 is never near a half
+      d[k] = fmaf(-31.f, qk, r);
+      r = qk;
+    }
+    d[0] = r;
+    const int e = j & 31, Rf = (e >> 2) & 3, slot = 32 * (j >> 5) + 8 * Rf + 2 * (e & 3) + (e >> 4);
+    const int mult = Rf == 0 ? 4 : (Rf == 1 ? 2 : (Rf == 2 ? 1 : -1));
     unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
 #pragma unroll
-    for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + j] = (unsigned char)(dig >> (8 * pl));
+    for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + slot] = (unsigned char)enc6((int)d[pl] * mult);
+    float kcs = Rf == 3 ? 0.125f * x : 0.f;                          // multiples of 1/8 below 2^21: exact
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1) kcs += __shfl_xor(kcs, off);
+    if (lane == 0 && hh < G) atomicAdd(&s_kc[hh], kcs);
   }
   lds_barrier();
 
@@ -289,28 +354,38 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     }
   }
   // ---- phase 1: visual scores, their min and max -------------------------
-  v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
-  if (rh < G) {
-    const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
-    const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
-    ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-    ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+  // K-side A operand of this lane: row (head rh, plane rp), k slots 32 g4 ..
+  // +31 as 32 dense 6-bit fields in 6 registers (zero rows past G)
+  v8i kdig = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+  {
+    const uint4* src = reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
+    const uint4 x0 = src[0], x1 = src[1];
+    const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    uint32_t o[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      const uint32_t c = (w[i >> 2] >> (8 * (i & 3))) & 0x3Fu;
+      const int bit = 6 * i, wd = bit >> 5, off = bit & 31;
+      o[wd] |= c << off;
+      if (off > 26) o[wd + 1] |= c >> (32 - off);
+    }
+    if (rh < G) kdig = v8i{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], 0, 0};
   }
-  const float inv2f = s_inv2f[oh < G ? oh : 0];
-  const float c0f = (float)s_c0[oh < G ? oh : 0];
-  // scores of this lane's 8 tokens (head oh) from one key tile; the same
-  // integer products and the same rounding in both passes
+  // scores of this lane's 8 tokens (head oh) from one key tile, in units of
+  // s = Q . c / 4 less the bit-3 constant: C[16 x 16] = A[16 x 128] B[128 x 16]
+  // with the 16x16x128 f8f6f4 product, A fp6 (e2m3) digits, B the key word
+  // masked in place into fp4 (e2m1) fields; the plane sums are exact and the
+  // same operations give the same scores in both passes
   auto scores = [&](const uint4& w0, const uint4& w1, float (&st)[8]) {
     const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      v4i acc = {0, 0, 0, 0};
-      acc = mfma(ak0, bits_lo(wd[m]), acc);
-      acc = mfma(ak1, bits_hi(wd[m]), acc);
-      // 2^3 Q . c = lo + 2^16 hi; both halves fit 31 bits, the sum is
-      // rounded to float (the same operations in both passes)
-      const int lo = acc[0] + (acc[1] << 8), hi = acc[2] + (acc[3] << 8);
-      st[m] = fmaf(fmaf((float)hi, 65536.f, (float)lo), inv2f, c0f);
+      const uint32_t w = wd[m];
+      const v8i bq{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
+                   (int)((w & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+      const v4f a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kdig, bq, v4f{0.f, 0.f, 0.f, 0.f}, 2, 4, 0,
+                                                                      127, 0, 127);
+      st[m] = fmaf(fmaf(fmaf(a[0], 31.f, a[1]), 31.f, a[2]), 31.f, a[3]);
       // pin the finished score: otherwise the compiler may keep the four
       // accumulator registers alive in its place
       asm volatile("" : "+v"(st[m]));
@@ -328,18 +403,11 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     kn1 = km1;
     load_k(nxt, km0, km1);                      // past the last tile: an in-bounds reread, unused
     // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
-    const bool ok = tile * kTile + 8 * i16 < n;
     float st[8];
     scores(kw0, kw1, st);
-    float tmin = st[0], tmax = st[0];
-#pragma unroll
-    for (int m = 1; m < 8; ++m) {
-      tmin = fminf(tmin, st[m]);
-      tmax = fmaxf(tmax, st[m]);
-    }
-    if (ok) {
-      vmin = fminf(vmin, tmin);
-      vmax = fmaxf(vmax, tmax);
+    if ((tile + 1) * kTile <= n || tile * kTile + 8 * i16 < n) {
+      vmin = min3f(min3f(vmin, st[0], st[1]), min3f(st[2], st[3], st[4]), min3f(st[5], st[6], st[7]));
+      vmax = max3f(max3f(vmax, st[0], st[1]), max3f(st[2], st[3], st[4]), max3f(st[5], st[6], st[7]));
     }
     // fold tile by tile: left free, the compiler sinks these updates past the
     // loop and keeps every tile's scores alive
@@ -356,11 +424,13 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   load_k(wave, kn0, kn1);
   // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
   // tokens whose p is 0: whatever codes they read, their digits are 0.
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vcb + (n > 0 ? (size_t)unit * R * 128 : 0)), (short)0,
+                                                    R * 512, kRsrcFlags);
+  const uint32_t voff = (uint32_t)(g4 * 128 + 8 * i16) * 4u;
   auto load_v = [&](int tile, uint4& w0, uint4& w1) {
-    const int row = max(min(tile * 4 + g4, R - 1), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
-    w0 = src[0];
-    w1 = src[1];
+    const uint32_t off = voff + (tile < ntiles ? (uint32_t)tile * 2048u : 0x80000000u);
+    w0 = ld_buf(rv, off);
+    w1 = ld_buf(rv, off + 16u);
   };
   uint4 vn0, vn1;
   load_v(wave, vn0, vn1);
@@ -403,22 +473,27 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       M = fmaxf(M, __shfl_xor(M, off));
       tmax = fmaxf(tmax, __shfl_xor(tmax, off));
     }
-    float lam = 1.f, mu = 0.f, vis_max = M;
+    // scores are in units of scale = 4 2^-F, offset by q . min_K plus the
+    // bit-3 constant; the exponent of a visual weight is lam s + mu
+    const double scale = ldexp(4.0, -s_F[hh]);
+    const double c0 = s_c0[hh] + (double)s_kc[hh] * scale;
+    double lam = scale, mu = -scale * (double)M, vis_max = (double)M * scale + c0;
     if (P.calib_on && n > 0) {
-      const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
-      lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
-      mu = t_lo - lam * m;
+      const double mr = (double)m * scale + c0, Mr = (double)M * scale + c0;
+      const double t_lo = (double)P.a_lo * mr + (double)P.c_lo, t_hi = (double)P.a_hi * Mr + (double)P.c_hi;
       // the largest value of g: the larger end of [t_lo, t_hi], or t_lo
       // when every score is the same (g is then the constant t_lo)
-      vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
+      vis_max = M > m ? fmax(t_lo, t_hi) : t_lo;
+      lam = M > m ? (t_hi - t_lo) / ((double)(M - m) * scale) * scale : 0.0;
+      mu = t_lo - vis_max - lam * (double)m;
     }
-    const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
+    const float top = fmaxf(n > 0 ? (float)vis_max : -INFINITY, tmax);
     if (lane == 0) {
       // visual weights relative to the largest one: p = 2^(s * lam' + mu');
       // alpha = its weight relative to the softmax reference
-      s_lam[hh] = lam * kLog2e;
-      s_mu[hh] = (mu - vis_max) * kLog2e;
-      s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
+      s_lam[hh] = (float)(lam * 1.4426950408889634);
+      s_mu[hh] = (float)(mu * 1.4426950408889634);
+      s_alpha[hh] = n > 0 ? exp2f(((float)vis_max - top) * kLog2e) : 0.f;
     }
     // tail probabilities (in place) and their sum
     float pt = 0.f;
@@ -615,9 +690,9 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
   __shared__ float s_q[4][128];
   __shared__ float s_qp[4][128];
   __shared__ double s_c0[4];
-  __shared__ float s_inv2f[4];
   __shared__ int s_F[4];
-  __shared__ __align__(16) uint32_t s_adig[4][4][32];
+  __shared__ __align__(16) uint32_t s_adig[4][4][32];   // fp6 digit codes: [head][plane][128 k slots]
+  __shared__ float s_kc[4];                              // per head: sum of Q / 8 over the bit-3 channels
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWavesL][4][2];
   __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
@@ -711,7 +786,10 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       s_next[0] = kAheadK * kWavesL;
       s_next[1] = kAheadV * kWavesL;
     }
-    if (tid < 4) s_psum[tid] = 0.0;
+    if (tid < 4) {
+      s_psum[tid] = 0.0;
+      s_kc[tid] = 0.f;
+    }
     for (int i = tid; i < 4 * 128; i += kThreadsL) (&s_vsum[0][0])[i] = 0ull;
 
     // ---- prologue (threads < 512: head ph, channel pj) ----------------------
@@ -746,19 +824,34 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
       const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
       int F = 0;
-      if (mq > 0.f) F = 21 - ilogbf(mq);
+      if (mq > 0.f) {
+        const int e = ilogbf(mq);
+        F = ldexpf(mq, 18 - e) > (float)kQMax ? 17 - e : 18 - e;
+      }
       s_F[tid] = F;
-      s_inv2f[tid] = ldexpf(1.f, -F - 3);
       s_c0[tid] = c0;
     }
     lds_barrier();
-    if (tid < 512) {
+    if (tid < 512) {                            // the digits of df_b1, formed the same way
       const int hh = tid >> 7, j = tid & 127;
-      const int Q = (int)rintf(ldexpf(s_qp[hh][j], s_F[hh]));
-      const uint32_t dig = cqm::sdigits((uint32_t)(Q * (1 << bit_weight(j & 31))));
+      const float x = rintf(ldexpf(s_qp[hh][j], s_F[hh]));
+      float d[4], r = x;
+#pragma unroll
+      for (int k = 3; k > 0; --k) {
+        const float qk = rintf(r * (1.f / 31.f));
+        d[k] = fmaf(-31.f, qk, r);
+        r = qk;
+      }
+      d[0] = r;
+      const int e = j & 31, Rf = (e >> 2) & 3, slot = 32 * (j >> 5) + 8 * Rf + 2 * (e & 3) + (e >> 4);
+      const int mult = Rf == 0 ? 4 : (Rf == 1 ? 2 : (Rf == 2 ? 1 : -1));
       unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
 #pragma unroll
-      for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + j] = (unsigned char)(dig >> (8 * pl));
+      for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + slot] = (unsigned char)enc6((int)d[pl] * mult);
+      float kcs = Rf == 3 ? 0.125f * x : 0.f;
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) kcs += __shfl_xor(kcs, off);
+      if (lane == 0 && hh < G) atomicAdd(&s_kc[hh], kcs);
     }
     lds_barrier();
 
@@ -807,15 +900,21 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
     }
 
     // ---- key pass: scores into LDS, their min and max --------------------------
-    v4i ak0 = {0, 0, 0, 0}, ak1 = {0, 0, 0, 0};
-    if (rh < G) {
-      const uint4 x0 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
-      const uint4 x1 = *reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4 + 4]);
-      ak0 = v4i{(int)x0.x, (int)x0.y, (int)x0.z, (int)x0.w};
-      ak1 = v4i{(int)x1.x, (int)x1.y, (int)x1.z, (int)x1.w};
+    v8i kdig = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    {
+      const uint4* src = reinterpret_cast<const uint4*>(&s_adig[rh][rp][8 * g4]);
+      const uint4 x0 = src[0], x1 = src[1];
+      const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+      uint32_t o[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t c = (w[i >> 2] >> (8 * (i & 3))) & 0x3Fu;
+        const int bit = 6 * i, wd = bit >> 5, off = bit & 31;
+        o[wd] |= c << off;
+        if (off > 26) o[wd + 1] |= c >> (32 - off);
+      }
+      if (rh < G) kdig = v8i{(int)o[0], (int)o[1], (int)o[2], (int)o[3], (int)o[4], (int)o[5], 0, 0};
     }
-    const float inv2f = s_inv2f[oh < G ? oh : 0];
-    const float c0f = (float)s_c0[oh < G ? oh : 0];
     float vmin = INFINITY, vmax = -INFINITY;
     // Slot j of the ring holds the key tile tq[j]; the slots are used in
     // turn, and a used slot is refilled in place with the next dealt tile.
@@ -833,12 +932,13 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       const uint32_t wd[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
       float st[8];
 #pragma unroll
-      for (int m = 0; m < 8; ++m) {
-        v4i acc = {0, 0, 0, 0};
-        acc = mfma(ak0, bits_lo(wd[m]), acc);
-        acc = mfma(ak1, bits_hi(wd[m]), acc);
-        const int lo = acc[0] + (acc[1] << 8), hi = acc[2] + (acc[3] << 8);
-        st[m] = fmaf(fmaf((float)hi, 65536.f, (float)lo), inv2f, c0f);
+      for (int m = 0; m < 8; ++m) {            // df_b1's scores, formed the same way
+        const uint32_t w = wd[m];
+        const v8i bq{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
+                     (int)((w & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+        const v4f a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kdig, bq, v4f{0.f, 0.f, 0.f, 0.f}, 2, 4, 0,
+                                                                        127, 0, 127);
+        st[m] = fmaf(fmaf(fmaf(a[0], 31.f, a[1]), 31.f, a[2]), 31.f, a[3]);
       }
       if (oh < G) {
         float4* dst = reinterpret_cast<float4*>(&s_sc[tile * kRegion + oh * 128 + 8 * i16]);
@@ -907,18 +1007,25 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
         M = fmaxf(M, __shfl_xor(M, off));
         tmax = fmaxf(tmax, __shfl_xor(tmax, off));
       }
-      float lam = 1.f, mu = 0.f, vis_max = M;
+      const double scale = ldexp(4.0, -s_F[hh]);   // the statistics of df_b1, computed the same way
+      const double c0 = s_c0[hh] + (double)s_kc[hh] * scale;
+      double lam = scale, mu = -scale * (double)M, vis_max = (double)M * scale + c0;
       if (P.calib_on && n > 0) {
-        const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
-        lam = M > m ? (t_hi - t_lo) / (M - m) : 0.f;
-        mu = t_lo - lam * m;
-        vis_max = M > m ? fmaxf(t_lo, t_hi) : t_lo;
+        // (the parameters pass through opaque copies: converted here rather
+        // than held in registers across the unit loop)
+        float alo = P.a_lo, clo = P.c_lo, ahi = P.a_hi, chi = P.c_hi;
+        asm volatile("" : "+s"(alo), "+s"(clo), "+s"(ahi), "+s"(chi));
+        const double mr = (double)m * scale + c0, Mr = (double)M * scale + c0;
+        const double t_lo = (double)alo * mr + (double)clo, t_hi = (double)ahi * Mr + (double)chi;
+        vis_max = M > m ? fmax(t_lo, t_hi) : t_lo;
+        lam = M > m ? (t_hi - t_lo) / ((double)(M - m) * scale) * scale : 0.0;
+        mu = t_lo - vis_max - lam * (double)m;
       }
-      const float top = fmaxf(n > 0 ? vis_max : -INFINITY, tmax);
+      const float top = fmaxf(n > 0 ? (float)vis_max : -INFINITY, tmax);
       if (lane == 0) {
-        s_lam[hh] = lam * kLog2e;
-        s_mu[hh] = (mu - vis_max) * kLog2e;
-        s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
+        s_lam[hh] = (float)(lam * 1.4426950408889634);
+        s_mu[hh] = (float)(mu * 1.4426950408889634);
+        s_alpha[hh] = n > 0 ? exp2f(((float)vis_max - top) * kLog2e) : 0.f;
       }
       float ptl = 0.f;
       for (int j = lane; j < T; j += 64) {

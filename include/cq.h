@@ -106,11 +106,14 @@ typedef struct {
  *                       multiple of 32, T <= 128: one launch of one 8-wave
  *                       workgroup per CU walking its units, the value pass of
  *                       one unit run beside the key pass of the next; the
- *                       keys are read once and the scores stay on chip.  The
- *                       key dot products take the query as four signed base-31
- *                       digits (about 20 bits, against 22 on the other fast
- *                       paths), so its results match CQ_PATH_FAST_ONE's to the
- *                       2e-3 tolerance, not bit for bit.  Needs no workspace. */
+ *                       keys are read once and the scores stay on chip.  Its
+ *                       key products give CQ_PATH_FAST_ONE's scores; its sums
+ *                       and tail are formed in another order, so its results
+ *                       match CQ_PATH_FAST_ONE's to the 2e-3 tolerance, not
+ *                       bit for bit.  Needs no workspace.
+ * At b = 1 the one-launch, LDS-score and pipelined paths take the query as
+ * four balanced base-31 digits (about 20 bits); the split path and b > 1 as a
+ * 22-bit fixed-point integer. */
 typedef enum {
   CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4,
   CQ_PATH_FAST_LDS = 5, CQ_PATH_FAST_PIPE = 6

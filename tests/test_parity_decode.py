@@ -234,7 +234,7 @@ def test_split_chunk_counts(splits):
     note(f"decode split chunks={splits}")
     got = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_SPLIT, splits, out_dtype=torch.float32)
     _compare(got, _oracle(K, V, q, kt, vt, 1, RELATIVE), 4)
-    base = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_ONE, out_dtype=torch.float32)
+    base = _run(K, V, q, kt, vt, 1, RELATIVE, cqb.CQ_PATH_FAST_SPLIT, 1, out_dtype=torch.float32)
     diff = float(np.max(np.abs(got - base)))
     assert diff <= 1e-5 * max(1.0, float(np.max(np.abs(base)))), f"max |diff| {diff:.3e}"
 

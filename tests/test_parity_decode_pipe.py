@@ -5,9 +5,9 @@ It reads every key tile once and keeps the visual scores on chip until the
 value tiles of the same slot use them, while the key tiles of the next
 (batch, kv head) unit stream in (QbitAI article on CalibQuant, "Method" parts
 2 and 3: post-scaled scores, the calibration map fixed by their min and max,
-post-scaled values).  Its outputs must be within 2e-3 of the oracle's; its
-query digits (about 20 bits) differ from the one-launch schedule's (22 bits),
-so the two agree only to that tolerance, not bit for bit.
+post-scaled values).  Its outputs must be within 2e-3 of the oracle's.  Its
+scores are the one-launch schedule's, but its sums and its text tail are
+formed in another order, so the two agree to that tolerance, not bit for bit.
 """
 import numpy as np
 import pytest
