@@ -144,41 +144,68 @@ def measured_traffic(workload, op):
 # CPU oracle leg
 # ---------------------------------------------------------------------------
 
-def cpu_baseline(cfg, K, V, q, kt, vt, sm, calib, budget_s):
-    """Time the oracle (as it stands) on whole (batch, kv head) units of the
-    same workload until ~budget_s seconds of CPU work; one sequence-step is
-    Hkv units."""
+def _oracle_unit(args):
+    """One (batch, kv head) unit through the oracle: quantize + pack K and V,
+    one calibrated decode.  Runs in a worker process; returns its seconds."""
+    Ku, Vu, qu, ktu, vtu, bits, sm, calib = args
     import numpy as np
     import oracle
     from threadpoolctl import threadpool_limits
-    G = cfg.Hq // cfg.Hkv
     c32 = oracle.Calib(*(float(np.float32(v)) for v in calib)) if calib else None
-    units, t_used = 0, 0.0
-    order = [(b, h) for b in range(cfg.B) for h in range(cfg.Hkv)]
-    rng = np.random.default_rng(0)
-    rng.shuffle(order)
-    for b, h in order:
-        Ku, Vu = K[b, h].cpu().numpy(), V[b, h].cpu().numpy()
-        limiter = threadpool_limits(limits=1)
-        qu = q[b, h * G:(h + 1) * G].cpu().numpy()
-        ktu = kt[b, h].cpu().numpy() if kt is not None else None
-        vtu = vt[b, h].cpu().numpy() if vt is not None else None
+    with threadpool_limits(limits=1):
         t0 = time.perf_counter()
-        kc, ks, km, _ = oracle.quantize_unit(Ku, cfg.bits)
-        vc, vs, vm, _ = oracle.quantize_unit(Vu, cfg.bits)
-        oracle.pack(kc, cfg.bits, "K")
-        oracle.pack(vc, cfg.bits, "V")
+        kc, ks, km, _ = oracle.quantize_unit(Ku, bits)
+        vc, vs, vm, _ = oracle.quantize_unit(Vu, bits)
+        oracle.pack(kc, bits, "K")
+        oracle.pack(vc, bits, "V")
         oracle.decode_unit(qu, kc, ks, km, vc, vs, vm, ktu, vtu, sm, c32)
-        t_used += time.perf_counter() - t0
-        limiter.restore_original_limits()
-        units += 1
-        if t_used >= budget_s:
-            break
-    seq_steps = units / cfg.Hkv
-    return {"value": seq_steps / t_used, "unit": "seq-steps/s", "cores": 1, "kind": "oracle",
-            "sample": f"{units} (batch, kv-head) units of {cfg.name} (n={cfg.n}, d={cfg.d}, fp16): quantize + pack "
-                      f"K and V and one {G}-head calibrated decode each, {t_used:.1f} s single-threaded; "
-                      f"{cfg.Hkv} units = 1 sequence-step"}
+        return time.perf_counter() - t0
+
+
+def _cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, K, V, q, kt, vt, sm, calib, budget_s):
+    """Time the oracle (as it stands) on whole (batch, kv head) units of the
+    same workload, one unit per task over a pool of worker processes (one
+    thread each, as many as the host's CPU share allows, at most 16), until
+    about budget_s seconds of CPU work are done; one sequence-step is Hkv
+    units.  The rate is units over the pool's wall-clock time."""
+    import multiprocessing as mp
+    import numpy as np
+    G = cfg.Hq // cfg.Hkv
+    workers = max(1, min(16, len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()))
+    order = [(b, h) for b in range(cfg.B) for h in range(cfg.Hkv)]
+    np.random.default_rng(0).shuffle(order)
+    # one probe unit fixes the sample size: about budget_s seconds of CPU work
+    def task(b, h):
+        return (K[b, h].cpu().numpy(), V[b, h].cpu().numpy(), q[b, h * G:(h + 1) * G].cpu().numpy(),
+                None if kt is None else kt[b, h].cpu().numpy(), None if vt is None else vt[b, h].cpu().numpy(),
+                cfg.bits, sm, calib)
+    _oracle_unit(task(*order[0]))                  # first call: imports and caches
+    probe = _oracle_unit(task(*order[0]))
+    units = int(min(len(order) - 1, max(workers, round(budget_s / max(probe, 1e-3)))))
+    units = max(workers, units - units % workers)
+    tasks = [task(b, h) for b, h in order[1:1 + units]]
+    ctx = mp.get_context("spawn")                  # the parent holds a GPU context: never fork it
+    with ctx.Pool(workers) as pool:
+        pool.map(_oracle_unit, tasks[:workers])    # workers started and warm before the clock
+        t0 = time.perf_counter()
+        cpu = sum(pool.map(_oracle_unit, tasks, chunksize=1))
+        wall = time.perf_counter() - t0
+    seq_steps = len(tasks) / cfg.Hkv
+    return {"value": seq_steps / wall, "unit": "seq-steps/s", "cores": workers, "kind": "oracle",
+            "cpu_model": _cpu_model(),
+            "sample": f"{len(tasks)} (batch, kv-head) units of {cfg.name} (n={cfg.n}, d={cfg.d}, fp16): quantize + "
+                      f"pack K and V and one {G}-head calibrated decode each; {workers} worker processes of one "
+                      f"thread, {wall:.1f} s wall, {cpu:.1f} s of CPU work; {cfg.Hkv} units = 1 sequence-step"}
 
 
 # ---------------------------------------------------------------------------
@@ -275,8 +302,9 @@ def run(args):
     cqb.cq_quantize_status(qws)
     if int(qws[4:8].view(torch.int32).item()) != 0:
         raise RuntimeError("a quantize call of the run timed out waiting; its codes were invalid")
-    tq = np.mean([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]) * 1e-3
-    td = np.mean([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]) * 1e-3
+    tq_all = np.array([ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]) * 1e-3
+    td_all = np.array([ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]) * 1e-3
+    tq, td = float(np.mean(tq_all)), float(np.mean(td_all))
     print(f"[bench] timed {args.steps} steps: {wall * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
     if args.only == "step":
         print(json.dumps({"workload": cfg.name, "steps": args.steps, "ms_per_step": wall * 1e3 / args.steps,
@@ -286,7 +314,7 @@ def run(args):
     # decode alone with the Infinity Cache flushed before every call
     scratch = Flush(dev)
     cold = []
-    for _ in range(max(10, args.steps)):
+    for _ in range(max(50, args.steps)):
         scratch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -294,7 +322,8 @@ def run(args):
         b.record(stream)
         cold.append((a, b))
     torch.cuda.synchronize()
-    td_cold = np.median([a.elapsed_time(b) for a, b in cold]) * 1e-3
+    tc_all = np.array([a.elapsed_time(b) for a, b in cold]) * 1e-3
+    td_cold = float(np.median(tc_all))
 
     # float16 unquantized baseline over the same n + T tokens, same flush
     Kf = torch.cat([K, kt], dim=2) if kt is not None else K
@@ -303,7 +332,7 @@ def run(args):
     fws = torch.empty(max(1, cqb.lib.cq_decode_attn_fp16_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n + cfg.T, cfg.d)),
                       dtype=torch.uint8, device=dev)
     fcold = []
-    for _ in range(max(10, args.steps)):
+    for _ in range(max(50, args.steps)):
         scratch()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record(stream)
@@ -321,6 +350,9 @@ def run(args):
         traffic = measured_traffic(cfg.name, op)
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic}
+
+    def pct(a):
+        return [round(float(np.percentile(a, p)) * 1e3, 4) for p in (10, 50, 90)]
 
     dominant = "quantize" if tq >= td else "decode"
     line = {
@@ -344,6 +376,8 @@ def run(args):
         "dominant_kernel": "cq_quantize_kv_pair" if dominant == "quantize" else "cq_decode_attn",
         "per_call_ms": {"quantize_kv_pair": round(tq * 1e3, 4), "decode_in_step": round(td * 1e3, 4),
                         "decode_cold": round(td_cold * 1e3, 4)},
+        "per_call_ms_p10_p50_p90": {"quantize_kv_pair": pct(tq_all), "decode_in_step": pct(td_all),
+                                    "decode_cold": pct(tc_all), "decode_cold_calls": len(tc_all)},
         "decode": {"seq_steps_per_s_cold": round(cfg.B / td_cold, 1),
                    "roofline_cold": roof(db, td_cold, "decode"),
                    "roofline_in_step": roof(db, td, "decode")},
@@ -598,7 +632,7 @@ def _rows(pattern):
     return rows
 
 
-def summarize(dirs, workload, command_note):
+def summarize(dirs, workload, command_note, profile_name=None):
     """Write profiles/<kernel>_<workload>.md from kernel-trace stats and
     counter CSVs, and profiles/traffic_<workload>.json with HBM bytes per launch
     scaled by the copy-kernel reference."""
@@ -625,8 +659,8 @@ def summarize(dirs, workload, command_note):
             cname = r.get("Counter_Name", r.get("Counter-Name", ""))
             val = float(r.get("Counter_Value", r.get("Counter-Value", 0)))
             per.setdefault((name, cname), []).append(val)
-        lines += ["## HBM counters (--pmc, KiB per dispatch, averaged)", "",
-                  "| kernel | counter | dispatches | avg KiB |", "|---|---|---|---|"]
+        lines += ["## Counters (--pmc, per dispatch, averaged; FETCH_SIZE / WRITE_SIZE in KiB)", "",
+                  "| kernel | counter | dispatches | avg |", "|---|---|---|---|"]
         for (name, cname), vals in sorted(per.items()):
             lines.append(f"| {name[:80]} | {cname} | {len(vals)} | {sum(vals) / len(vals):.1f} |")
         lines.append("")
@@ -635,8 +669,9 @@ def summarize(dirs, workload, command_note):
         ref_bytes = (1 << 29) * 2
         f_read = (sum(copy_read) / len(copy_read) * 1024 / ref_bytes) if copy_read else None
         f_write = (sum(copy_write) / len(copy_write) * 1024 / ref_bytes) if copy_write else None
-        lines += [f"Copy-kernel reference (1 GiB read + 1 GiB written): FETCH_SIZE factor "
-                  f"{f_read}, WRITE_SIZE factor {f_write} (counter KiB x 1024 / true bytes).", ""]
+        if f_read or f_write:
+            lines += [f"Copy-kernel reference (1 GiB read + 1 GiB written): FETCH_SIZE factor "
+                      f"{f_read}, WRITE_SIZE factor {f_write} (counter KiB x 1024 / true bytes).", ""]
 
         def op_bytes(kernels):
             # one call launches each kernel in `kernels` once: sum their per-dispatch averages
@@ -653,7 +688,7 @@ def summarize(dirs, workload, command_note):
             if b is not None:
                 traffic[op] = {"bytes_per_launch": round(b), "kernels": list(kernels),
                                "source_digest": source_digest(*KERNEL_SOURCES[op])}
-    name = "summary" if not stats else "kernels"
+    name = profile_name or ("summary" if not stats else "kernels")
     with open(os.path.join(PROFILES, f"{name}_{workload}.md"), "w") as fh:
         fh.write("\n".join(lines) + "\n")
     if traffic:
@@ -677,9 +712,10 @@ def main():
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
     ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream"], default=None)
     ap.add_argument("--command-note", default="")
+    ap.add_argument("--profile-name", default=None, help="profiles/<name>_<workload>.md for --summarize")
     args = ap.parse_args()
     if args.summarize:
-        summarize(args.summarize, args.workload, args.command_note)
+        summarize(args.summarize, args.workload, args.command_note, args.profile_name)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
