@@ -29,7 +29,12 @@ Sweeps (not the headline line; one JSON line per point, then a table):
                            stream: chunked prefill of the long-context
                            cache (range updates per 512/2048-token chunk,
                            final codes, eager codes) against the one-shot
-                           quantization.  No name: all four
+                           quantization;
+                           tail: the B=64 n=8192 decode at text-tail
+                           lengths 64 .. 4096;
+                           shapes: quantize and decode of the one-layer
+                           workloads (B=16 n=3328 and B=64 n=8192) on their
+                           own.  No name: all six
 
 Profiling helpers (used to produce profiles/):
     --only {step,decode,copy}
@@ -432,7 +437,7 @@ def sweeps(args):
         rows.append(row)
         print(json.dumps(row), flush=True)
 
-    which = set(args.sweeps) or {"bits", "budget", "graph", "stream"}
+    which = set(args.sweeps) or {"bits", "budget", "graph", "stream", "tail", "shapes"}
     layers, Hq, Hkv, d, T = 32, 32, 8, 128, 64
     calib = (0.9, 0.0, 0.8, 0.0)
 
@@ -471,6 +476,73 @@ def sweeps(args):
               "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
         del K, V, kt, vt, q, out, Kf, Vf, fws, scratch
         torch.cuda.empty_cache()
+
+    def tail_sweep():
+        """B=64, n=8192, one layer, decode with the Infinity Cache flushed at
+        text-tail lengths on both sides of the fused pass's 256 tokens"""
+        scratch = Flush(dev)
+        base = CONFIGS["long_n8192"]
+        K = kv_torch(base.seed, 0, ROLE_K, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+        V = kv_torch(base.seed, 0, ROLE_V, base.B, base.Hkv, base.n, base.d, base.dtype, dev)
+        q = q_torch(base.seed, 0, base.B, base.Hq, base.d, base.dtype, dev)
+        kc, ks, km = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
+        vc, vs, vm = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
+        del K, V
+        out = torch.empty((base.B, base.Hq, base.d), dtype=torch.float16, device=dev)
+        for T_ in (64, 256, 257, 1024, 4096):
+            cfg = Config(f"long_n8192_T{T_}", B=base.B, Hq=base.Hq, Hkv=base.Hkv, n=base.n, T=T_, seed=base.seed)
+            note(f"tail sweep T={T_}")
+            kt = kv_torch(base.seed, 0, ROLE_KTAIL, base.B, base.Hkv, T_, base.d, base.dtype, dev)
+            vt = kv_torch(base.seed, 0, ROLE_VTAIL, base.B, base.Hkv, T_, base.d, base.dtype, dev)
+            ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, T_, cfg.d, 1)),
+                             dtype=torch.uint8, device=dev)
+            t = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=1, sm_scale=sm,
+                                                 calib=cfg.calib, out=out, workspace=ws), args.steps, scratch)
+            nb = decode_bytes(cfg)
+            emit({"sweep": "tail", "B": cfg.B, "n": cfg.n, "T": T_, "decode_ms": round(t * 1e3, 4),
+                  "seq_steps_per_s": round(cfg.B / t, 1), "GBs": round(nb / t / 1e9, 1),
+                  "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
+            del kt, vt, ws
+        del kc, ks, km, vc, vs, vm, q, out, scratch
+        torch.cuda.empty_cache()
+
+    def shapes_sweep():
+        """the single-layer workloads on their own: quantize of K and V, and one
+        decode with the Infinity Cache flushed"""
+        scratch = Flush(dev)
+        for name in ("internvl8b_n3328", "long_n8192"):
+            cfg = CONFIGS[name]
+            note(f"shapes {name}")
+            K = kv_torch(cfg.seed, 0, ROLE_K, cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.dtype, dev)
+            V = kv_torch(cfg.seed, 0, ROLE_V, cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.dtype, dev)
+            kt = kv_torch(cfg.seed, 0, ROLE_KTAIL, cfg.B, cfg.Hkv, cfg.T, cfg.d, cfg.dtype, dev)
+            vt = kv_torch(cfg.seed, 0, ROLE_VTAIL, cfg.B, cfg.Hkv, cfg.T, cfg.d, cfg.dtype, dev)
+            q = q_torch(cfg.seed, 0, cfg.B, cfg.Hq, cfg.d, cfg.dtype, dev)
+            kw = cqb.code_words_shape(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits, cqb.CQ_LAYOUT_K)
+            vw = cqb.code_words_shape(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits, cqb.CQ_LAYOUT_V)
+            f32 = dict(dtype=torch.float32, device=dev)
+            kc, vc = torch.empty(kw, dtype=torch.int32, device=dev), torch.empty(vw, dtype=torch.int32, device=dev)
+            ks, km, vs, vm = (torch.empty((cfg.B, cfg.Hkv, cfg.d), **f32) for _ in range(4))
+            qws = torch.zeros(max(256, cqb.lib.cq_quantize_kv_pair_workspace(cfg.B, cfg.Hkv, cfg.n, cfg.d, cfg.bits)),
+                              dtype=torch.uint8, device=dev)
+            tq = timed(lambda: cqb.cq_quantize_kv_pair(K, V, cfg.bits, k_out=(kc, ks, km), v_out=(vc, vs, vm),
+                                                       workspace=qws), args.steps, scratch)
+            cqb.cq_quantize_status(qws)
+            out = torch.empty((cfg.B, cfg.Hq, cfg.d), dtype=torch.float16, device=dev)
+            ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(cfg.B, cfg.Hq, cfg.Hkv, cfg.n, cfg.T, cfg.d,
+                                                                     cfg.bits)), dtype=torch.uint8, device=dev)
+            td = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=cfg.n, bits=cfg.bits,
+                                                  sm_scale=sm, calib=cfg.calib, out=out, workspace=ws),
+                       args.steps, scratch)
+            qb, db = 2 * quant_bytes(cfg), decode_bytes(cfg)
+            emit({"sweep": "shapes", "workload": name, "B": cfg.B, "n": cfg.n, "T": cfg.T,
+                  "quantize_ms": round(tq * 1e3, 4), "quantize_GBs": round(qb / tq / 1e9, 1),
+                  "quantize_frac_8TBs": round(qb / tq / 1e9 / HBM_PEAK_GBS, 4),
+                  "decode_ms": round(td * 1e3, 4), "decode_seq_steps_per_s": round(cfg.B / td, 1),
+                  "decode_GBs": round(db / td / 1e9, 1), "decode_frac_8TBs": round(db / td / 1e9 / HBM_PEAK_GBS, 4)})
+            del K, V, kt, vt, q, kc, vc, ks, km, vs, vm, qws, out, ws
+            torch.cuda.empty_cache()
+        del scratch
 
     def budget_sweep():
         """32 layers, the largest batch whose cache fits the budget"""
@@ -601,6 +673,10 @@ def sweeps(args):
         budget_sweep()
     if "graph" in which:
         graph_sweep()
+    if "tail" in which:
+        tail_sweep()
+    if "shapes" in which:
+        shapes_sweep()
     if "stream" in which:
         stream_sweep()
 
@@ -614,6 +690,14 @@ def sweeps(args):
             pt, ms = f"{r['layers']} layers, n={r['n']}, {r['mode']}", r["step_ms"]
         elif r["sweep"] == "stream":
             pt, ms = f"{r['mode']}, chunk {r['chunk']}, n={r['n']}", r["ms"]
+        elif r["sweep"] == "tail":
+            pt, ms = f"T={r['T']}, n={r['n']}", r["decode_ms"]
+        elif r["sweep"] == "shapes":
+            print(f"| shapes | {r['workload']} quantize | {r['B']} | {r['quantize_ms']} | - | {r['quantize_GBs']} | "
+                  f"{r['quantize_frac_8TBs']} |", file=sys.stderr)
+            print(f"| shapes | {r['workload']} decode | {r['B']} | {r['decode_ms']} | {r['decode_seq_steps_per_s']} | "
+                  f"{r['decode_GBs']} | {r['decode_frac_8TBs']} |", file=sys.stderr)
+            continue
         else:
             pt, ms = f"{r['budget_GiB']} GiB, n={r['n']}, {r['cache']}", r["step_ms"]
         print(f"| {r['sweep']} | {pt} | {r['B']} | {ms} | {r['seq_steps_per_s']} | {r['GBs']} | {r['frac_8TBs']} |",
@@ -710,7 +794,8 @@ def main():
                                                              "generic"],
                     help="decode schedule for --only decode")
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
-    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream"], default=None)
+    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream", "tail", "shapes"],
+                    default=None)
     ap.add_argument("--command-note", default="")
     ap.add_argument("--profile-name", default=None, help="profiles/<name>_<workload>.md for --summarize")
     args = ap.parse_args()

@@ -133,14 +133,155 @@ struct Params {
   float a_lo, c_lo, a_hi, c_hi;
 };
 
+// A text tail longer than the fused pass takes (T > kMaxTail), for one unit,
+// run by the 8 waves of its workgroup after its visual sums are done, in
+// chunks of kMaxTail tokens with a running reference (online softmax):
+//   m = max_t s_t so far;  acc = sum_t exp(s_t - m) vt_t;  pt = sum_t exp(s_t - m),
+// rescaled by exp(m_old - m_new) when a chunk raises m (the text tail is not
+// quantized: "Method" part 2 applies to the visual cache only, per the
+// abstract).  Leaves sum_t exp(s_t - m) vt_t per (phase, head, channel) in
+// s_tailred, the sums in s_ptail and m in s_tm.  Chunk scores: thread (token
+// 4 wave + lane / 16 + 32 r, channels 8 (lane % 16) ..); chunk values: thread
+// (channel pair tid % 64, tokens tid / 64 + 8 i).
+template <int G, bool F32>
+__device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128], float (&s_ts)[4][kMaxTail],
+                          float (&s_tailred)[kThreads / 64][4][128], float* s_ptail, float* s_tm, float* s_cm,
+                          float* s_cs) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sub = lane >> 4, cl = lane & 15, vcp = tid & 63, vph = tid >> 6;
+  const int T = P.T;
+  constexpr int kRounds = kMaxTail / (4 * kWaves);              // 8 score rounds of 32 tokens
+  constexpr int kVals = kMaxTail / kWaves;                      // 32 value tokens per thread
+  const char* ktb = reinterpret_cast<const char*>(P.kt);
+  const char* vtb = reinterpret_cast<const char*>(P.vt);
+  float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, pt[4] = {0.f, 0.f, 0.f, 0.f};
+  float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+  for (int c0 = 0; c0 < T; c0 += kMaxTail) {
+    // this chunk's value inputs are requested first, then its keys (rows
+    // past T read the last row: clamped, and their weights are 0)
+    uint32_t vr[kVals][F32 ? 2 : 1];
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) {
+      const size_t e = ((size_t)unit * T + min(c0 + vph + kWaves * i, T - 1)) * 128 + 2 * vcp;
+      if constexpr (F32) {
+        const uint2 x = *reinterpret_cast<const uint2*>(vtb + e * 4);
+        vr[i][0] = x.x;
+        vr[i][F32 ? 1 : 0] = x.y;
+      } else {
+        vr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vtb + e * 2));
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+      const int j = c0 + 4 * wave + sub + 4 * kWaves * r;
+      const size_t e = ((size_t)unit * T + min(j, T - 1)) * 128 + 8 * cl;
+      float kf[8];
+      if constexpr (F32) {
+        const uint4* src = reinterpret_cast<const uint4*>(ktb + e * 4);
+        const uint4 x0 = cqd::ld_nt(src), x1 = cqd::ld_nt(src + 1);
+        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int c = 0; c < 8; ++c) kf[c] = __uint_as_float(w[c]);
+      } else {
+        const uint4 x = cqd::ld_nt(reinterpret_cast<const __half*>(ktb + e * 2));
+        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(w[c] & 0xFFFF)));
+          kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(w[c] >> 16)));
+        }
+      }
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        float sc = 0.f;
+#pragma unroll
+        for (int c = 0; c < 8; ++c) sc = fmaf(s_q[hh][8 * cl + c], kf[c], sc);
+        sc += __shfl_xor(sc, 8);
+        sc += __shfl_xor(sc, 4);
+        sc += __shfl_xor(sc, 2);
+        sc += __shfl_xor(sc, 1);
+        if (cl == 0) s_ts[hh][j - c0] = j < T ? sc : -INFINITY;
+      }
+    }
+    cqm::lds_barrier();
+    if (wave < G) {                               // wave hh: the chunk's largest score
+      const int hh = wave;
+      float cm = -INFINITY;
+      for (int t = lane; t < kMaxTail; t += 64) cm = fmaxf(cm, s_ts[hh][t]);
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+      if (lane == 0) s_cm[hh] = cm;
+    }
+    cqm::lds_barrier();
+    float m_new[4], rs[4];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      m_new[hh] = fmaxf(m_run[hh], s_cm[hh]);
+      rs[hh] = exp2f((m_run[hh] - m_new[hh]) * kLog2e);       // 0 for the first chunk
+    }
+    if (wave < G) {                               // wave hh: weights in place, their sum
+      const int hh = wave;
+      float cs = 0.f;
+      for (int t = lane; t < kMaxTail; t += 64) {
+        const float pw = exp2f((s_ts[hh][t] - m_new[hh]) * kLog2e);   // 0 past T
+        s_ts[hh][t] = pw;
+        cs += pw;
+      }
+#pragma unroll
+      for (int off = 32; off > 0; off >>= 1) cs += __shfl_xor(cs, off);
+      if (lane == 0) s_cs[hh] = cs;
+    }
+    cqm::lds_barrier();
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      ta[hh][0] *= rs[hh];
+      ta[hh][1] *= rs[hh];
+      pt[hh] = pt[hh] * rs[hh] + s_cs[hh];
+      m_run[hh] = m_new[hh];
+    }
+#pragma unroll
+    for (int i = 0; i < kVals; ++i) {
+      float v0, v1;
+      if constexpr (F32) {
+        v0 = __uint_as_float(vr[i][0]);
+        v1 = __uint_as_float(vr[i][F32 ? 1 : 0]);
+      } else {
+        v0 = __half2float(__ushort_as_half((unsigned short)(vr[i][0] & 0xFFFF)));
+        v1 = __half2float(__ushort_as_half((unsigned short)(vr[i][0] >> 16)));
+      }
+      const int t = vph + kWaves * i;
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh) {
+        ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
+        ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+      }
+    }
+    cqm::lds_barrier();                           // the chunk's weights are read before the next scores
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    s_tailred[vph][hh][2 * vcp] = ta[hh][0];
+    s_tailred[vph][hh][2 * vcp + 1] = ta[hh][1];
+  }
+  if (tid < G) {
+    s_ptail[tid] = pt[tid];
+    s_tm[tid] = m_run[tid];
+  }
+}
+
 // F32: query and text tail are float32 (else float16); the fast path takes
 // them in one dtype.
-template <int G, bool F32>
+// LT: the text tail is longer than kMaxTail (a separate instance, so that the
+// chunked tail's registers do not weigh on the kernel of the common case)
+template <int G, bool F32, bool LT>
 __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int unit = blockIdx.x;
   const int b = unit / P.Hkv, h = unit % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = P.n, T = P.T;
+  // the text tail in the fused pass (scores beside the prologue, values
+  // beside the value pass); a longer one runs in chunks at the end
+  const int Tf = LT ? 0 : T;
   const int ntiles = (n + kTile - 1) / kTile;
   const int R = n >> 5;
   // Issue priority: the two workgroups on a CU would otherwise run their key
@@ -159,6 +300,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
+  __shared__ float s_vmax[4], s_tm[4], s_cm[4], s_cs[4];   // visual max, tail reference; long-tail chunk max / sum
   __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
   __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
@@ -323,7 +465,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
         s += __shfl_xor(s, 4);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 1);
-        if (cl == 0 && j < T) s_ts[hh][j] = s;
+        if (cl == 0 && j < Tf) s_ts[hh][j] = s;
       }
     };
 #pragma unroll
@@ -344,7 +486,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       }
       tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
     }
-    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < T; j0 += 4 * kWaves) {
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves) {
       const int j = j0 + sub;
       float kf[8];
 #pragma unroll
@@ -466,7 +608,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
     float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
     float tmax = -INFINITY;
-    for (int j = lane; j < T; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
+    for (int j = lane; j < Tf; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       m = fminf(m, __shfl_xor(m, off));
@@ -494,10 +636,12 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       s_lam[hh] = (float)(lam * 1.4426950408889634);
       s_mu[hh] = (float)(mu * 1.4426950408889634);
       s_alpha[hh] = n > 0 ? exp2f(((float)vis_max - top) * kLog2e) : 0.f;
+      s_vmax[hh] = n > 0 ? (float)vis_max : -INFINITY;
+      s_tm[hh] = top;                           // the fused tail's weights are taken relative to top
     }
     // tail probabilities (in place) and their sum
     float pt = 0.f;
-    for (int j = lane; j < T; j += 64) {
+    for (int j = lane; j < Tf; j += 64) {
       const float pj = exp2f((s_ts[hh][j] - top) * kLog2e);
       s_ts[hh][j] = pj;
       pt += pj;
@@ -514,7 +658,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
       const int t = vph + kPhases * i;
-      if (t < T) {
+      if (t < Tf) {
         float v0, v1;
         if constexpr (F32) {
           v0 = __uint_as_float(vtr[i][0]);
@@ -530,7 +674,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
         }
       }
     }
-    for (int t = kPreTail + vph; t < T; t += kPhases) {
+    for (int t = kPreTail + vph; t < Tf; t += kPhases) {
       const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
       const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
 #pragma unroll
@@ -637,6 +781,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
   lds_barrier();
+  if constexpr (LT) {
+    long_tail<G, F32>(P, unit, s_q, s_ts, s_tailred, s_ptail, s_tm, s_cm, s_cs);
+    lds_barrier();
+  }
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     const float sv = (float)((double)(long long)s_vsum[hh][j] * (1.0 / 1073741824.0));   // 2^-30
@@ -645,12 +793,20 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
 #pragma unroll
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
     const float pt = s_ptail[hh];
-    // the visual sums are relative to the largest visual probability,
-    // alpha = exp(visual max - softmax max) relative to the reference
-    const float al = s_alpha[hh];
-    float o = tail;
+    // the visual sums are relative to the largest visual weight, the tail's
+    // to its reference (top in the fused pass, the tail's own largest score
+    // in the chunked one): each part is weighed by exp(its reference - top),
+    // top the larger of the two (in the fused pass the tail's factor is 1 and
+    // the visual one alpha)
+    const float vx = s_vmax[hh], tx = s_tm[hh], top = fmaxf(vx, tx);
+    const float al = n > 0 ? exp2f((vx - top) * kLog2e) : 0.f;
+    const float at = exp2f((tx - top) * kLog2e);
+    // (the tail terms are pinned, so that the fused multiply-adds are the
+    // LDS-score kernel's, whose results equal these bit for bit)
+    float o = at * tail, ptw = at * pt;
+    asm volatile("" : "+v"(o), "+v"(ptw));
     if (n > 0) o += al * (s_vs[j] * sv + pv * s_vm[j]);
-    o /= (al * pv + pt);
+    o /= (al * pv + ptw);
     const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
     if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
     else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);
@@ -1212,7 +1368,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 // For b = 8 a code (0..255) is not a signed byte: it enters as its low nibble
 // plus twice (8 x high nibble), three products into the same accumulator.
 // The key dot product can exceed 32 bits for b >= 4 and is summed in 64 bits.
-template <int BITS, int G, bool F32>
+template <int BITS, int G, bool F32, bool LT>
 __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   constexpr int E = 32 / BITS;                  // codes per word
   constexpr int TB = 4 * E;                     // tokens per tile
@@ -1223,6 +1379,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   const int b = unit / P.Hkv, h = unit % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = P.n, T = P.T;
+  const int Tf = LT ? 0 : T;                   // the text tail in the fused pass (else chunked at the end)
   const int tiles = (n + TB - 1) / TB;
   const int R = n / E;
 
@@ -1236,6 +1393,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ float s_ts[4][kMaxTail];
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
+  __shared__ float s_vmax[4], s_tm[4], s_cm[4], s_cs[4];
   __shared__ float s_tailred[kThreads / 64][4][128];
   __shared__ float s_vred[kWaves][4][128];
   __shared__ float s_psum[kWaves][4];
@@ -1443,7 +1601,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
         s += __shfl_xor(s, 4);
         s += __shfl_xor(s, 2);
         s += __shfl_xor(s, 1);
-        if (cl == 0 && j < T) s_ts[hh][j] = s;
+        if (cl == 0 && j < Tf) s_ts[hh][j] = s;
       }
     };
 #pragma unroll
@@ -1464,7 +1622,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       }
       tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
     }
-    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < T; j0 += 4 * kWaves) {
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves) {
       const int j = j0 + sub;
       float kf[8];
 #pragma unroll
@@ -1489,7 +1647,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     float m = lane < kWaves ? s_red[lane][hh][0] : INFINITY;
     float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
     float tmax = -INFINITY;
-    for (int j = lane; j < T; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
+    for (int j = lane; j < Tf; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) {
       m = fminf(m, __shfl_xor(m, off));
@@ -1512,10 +1670,12 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       s_lam[hh] = lam * kLog2e;
       s_mu[hh] = (mu - vis_max) * kLog2e;
       s_alpha[hh] = n > 0 ? exp2f((vis_max - top) * kLog2e) : 0.f;
+      s_vmax[hh] = n > 0 ? vis_max : -INFINITY;
+      s_tm[hh] = top;
     }
     // tail probabilities (in place) and their sum
     float pt = 0.f;
-    for (int j = lane; j < T; j += 64) {
+    for (int j = lane; j < Tf; j += 64) {
       const float pj = exp2f((s_ts[hh][j] - top) * kLog2e);
       s_ts[hh][j] = pj;
       pt += pj;
@@ -1532,7 +1692,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
       const int t = vph + kPhases * i;
-      if (t < T) {
+      if (t < Tf) {
         float v0, v1;
         if constexpr (F32) {
           v0 = __uint_as_float(vtr[i][0]);
@@ -1548,7 +1708,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
         }
       }
     }
-    for (int t = kPreTail + vph; t < T; t += kPhases) {
+    for (int t = kPreTail + vph; t < Tf; t += kPhases) {
       const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
       const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
 #pragma unroll
@@ -1651,6 +1811,10 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
   lds_barrier();
+  if constexpr (LT) {
+    long_tail<G, F32>(P, unit, s_q, s_ts, s_tailred, s_ptail, s_tm, s_cm, s_cs);
+    lds_barrier();
+  }
   if (tid < G * 128) {
     const int hh = tid >> 7, j = tid & 127;
     float sv = 0.f, pv = 0.f;
@@ -1662,10 +1826,13 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     float tail = 0.f;
 #pragma unroll
     for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
-    const float pt = s_ptail[hh], al = s_alpha[hh];
-    float o = tail;
+    // each part weighed by exp(its reference - top), as in the 1-bit kernel
+    const float pt = s_ptail[hh];
+    const float vx = s_vmax[hh], tx = s_tm[hh], top = fmaxf(vx, tx);
+    const float al = n > 0 ? exp2f((vx - top) * kLog2e) : 0.f, at = exp2f((tx - top) * kLog2e);
+    float o = at * tail;
     if (n > 0) o += al * (P.vs[(size_t)unit * 128 + j] * sv + pv * P.vm[(size_t)unit * 128 + j]);
-    o /= (al * pv + pt);
+    o /= (al * pv + at * pt);
     const size_t oi = ((size_t)b * P.Hq + h * G + hh) * 128 + j;
     if (P.out_f32) reinterpret_cast<float*>(P.out)[oi] = o;
     else reinterpret_cast<__half*>(P.out)[oi] = __float2half_rn(o);
@@ -1674,12 +1841,17 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
 
 
 
+template <bool F32, bool LT>
+hipError_t launch_f1(const Params& p, int G, int units, hipStream_t st) {
+  if (G == 1) { CQ_LAUNCH((df_b1<1, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_b1<2, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_b1<4, F32, LT>), dim3(units), dim3(kThreads), 0, st, p);
+  return hipSuccess;
+}
+
 template <bool F32>
 hipError_t launch_f(const Params& p, int G, int units, hipStream_t st) {
-  if (G == 1) { CQ_LAUNCH((df_b1<1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  if (G == 2) { CQ_LAUNCH((df_b1<2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  CQ_LAUNCH((df_b1<4, F32>), dim3(units), dim3(kThreads), 0, st, p);
-  return hipSuccess;
+  return p.T > kMaxTail ? launch_f1<F32, true>(p, G, units, st) : launch_f1<F32, false>(p, G, units, st);
 }
 
 // Co-resident workgroups of an LDS-score kernel on the current device.
@@ -1711,12 +1883,17 @@ hipError_t launch_l(const Params& p, int G, int units, hipStream_t st) {
   return launch_l1<4, F32>(p, units, st);
 }
 
+template <int BITS, bool F32, bool LT>
+hipError_t launch_bn1(const Params& p, int G, int units, hipStream_t st) {
+  if (G == 1) { CQ_LAUNCH((df_bn<BITS, 1, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_bn<BITS, 2, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_bn<BITS, 4, F32, LT>), dim3(units), dim3(kThreads), 0, st, p);
+  return hipSuccess;
+}
+
 template <int BITS, bool F32>
 hipError_t launch_bn(const Params& p, int G, int units, hipStream_t st) {
-  if (G == 1) { CQ_LAUNCH((df_bn<BITS, 1, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  if (G == 2) { CQ_LAUNCH((df_bn<BITS, 2, F32>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  CQ_LAUNCH((df_bn<BITS, 4, F32>), dim3(units), dim3(kThreads), 0, st, p);
-  return hipSuccess;
+  return p.T > kMaxTail ? launch_bn1<BITS, F32, true>(p, G, units, st) : launch_bn1<BITS, F32, false>(p, G, units, st);
 }
 
 template <bool F32>
@@ -1735,8 +1912,7 @@ size_t decode_fast_ws(int, int, int, int, int, int) { return 0; }
 bool decode_fast_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
   return (a.bits == 1 || a.bits == 2 || a.bits == 4 || a.bits == 8) && a.d == 128 &&
-         (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && a.T <= kMaxTail &&
-         (a.T == 0 || a.tail_dtype == a.q_dtype);
+         (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && (a.T == 0 || a.tail_dtype == a.q_dtype);
 }
 
 bool decode_lds_supported(const DecodeArgs& a) {

@@ -22,9 +22,9 @@ def fast_ok(q, K, kt, bits, path=cqb.CQ_PATH_FAST):
     """Shapes the matrix-core decode schedules take (else CQ_ERR_UNSUPPORTED)."""
     n, G = K.shape[2], q.shape[1] // K.shape[1]
     T = 0 if kt is None else kt.shape[2]
-    common = G in (1, 2, 4) and n % 32 == 0 and T <= 256 and (T == 0 or kt.dtype == q.dtype)
-    one = common
-    split = common and bits == 1 and n > 0
+    common = G in (1, 2, 4) and n % 32 == 0 and (T == 0 or kt.dtype == q.dtype)
+    one = common                        # any text-tail length: a long one is taken in chunks
+    split = common and bits == 1 and n > 0 and T <= 256
     return {cqb.CQ_PATH_FAST_ONE: one, cqb.CQ_PATH_FAST_SPLIT: split}.get(path, one or split)
 
 

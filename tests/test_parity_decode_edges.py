@@ -127,13 +127,13 @@ def _dev(a):
 
 def _takes(path, bits, G, n, T):
     """Whether a forced path takes the shape (else the library returns CQ_ERR_UNSUPPORTED)."""
-    fast = G in (1, 2, 4) and n % 32 == 0 and T <= 256
+    fast = G in (1, 2, 4) and n % 32 == 0
     if path == P.CQ_PATH_FAST_ONE:
         return fast
     if path == P.CQ_PATH_FAST_SPLIT:
-        return fast and bits == 1 and n > 0
+        return fast and bits == 1 and n > 0 and T <= 256
     if path == P.CQ_PATH_FAST_LDS:
-        return fast and bits == 1 and G * -(-n // 128) <= 256
+        return fast and bits == 1 and G * -(-n // 128) <= 256 and T <= 256
     if path == P.CQ_PATH_FAST_PIPE:
         return fast and bits == 1 and 32 <= n <= 8192 and T <= 128
     return True
