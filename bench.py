@@ -791,7 +791,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--only", choices=["step", "decode", "copy"], default=None)
     ap.add_argument("--path", default="auto", choices=["auto", "fast", "fast_one", "fast_lds", "fast_pipe", "fast_split",
-                                                             "generic"],
+                                                       "fast_wide", "generic"],
                     help="decode schedule for --only decode")
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
     ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream", "tail", "shapes"],

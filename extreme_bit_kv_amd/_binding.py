@@ -29,8 +29,8 @@ lib = ctypes.CDLL(LIB_PATH)
 CQ_OK, CQ_ERR_INVALID_ARG, CQ_ERR_UNSUPPORTED, CQ_ERR_WORKSPACE, CQ_ERR_HIP, CQ_ERR_TIMEOUT = range(6)
 CQ_F16, CQ_F32 = 0, 1
 CQ_LAYOUT_K, CQ_LAYOUT_V = 0, 1
-CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT, CQ_PATH_FAST_LDS, CQ_PATH_FAST_PIPE = (
-    0, 1, 2, 3, 4, 5, 6)
+(CQ_PATH_AUTO, CQ_PATH_GENERIC, CQ_PATH_FAST, CQ_PATH_FAST_ONE, CQ_PATH_FAST_SPLIT, CQ_PATH_FAST_LDS, CQ_PATH_FAST_PIPE,
+ CQ_PATH_FAST_WIDE) = range(8)
 
 EXPORTED = ("cq_abi_version", "cq_last_hip_error", "cq_status_str", "cq_quantize_kv_workspace", "cq_quantize_kv",
             "cq_decode_attn_workspace", "cq_decode_attn", "cq_visual_scores", "cq_calibrate",
@@ -45,7 +45,8 @@ class cq_calib(ctypes.Structure):
 
 
 class cq_opts(ctypes.Structure):
-    _fields_ = [("path", ctypes.c_int32), ("splits", ctypes.c_int32), ("max_polls", ctypes.c_int32)]
+    _fields_ = [("path", ctypes.c_int32), ("splits", ctypes.c_int32), ("max_polls", ctypes.c_int32),
+                ("n_cap", ctypes.c_int32)]
 
 
 _i32, _sz, _vp, _f32 = ctypes.c_int32, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
@@ -193,8 +194,9 @@ def cq_quantize_kv(x, bits: int, layout: int, codes=None, scale=None, minv=None,
 
 
 def _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, n, bits, out,
-                    out_dtype):
-    """Checks of the decode operands; returns (B, Hq, Hkv, T, d, tail dtype code, out, leading C args)."""
+                    out_dtype, n_cap=0):
+    """Checks of the decode operands; returns (B, Hq, Hkv, T, d, tail dtype code, out, leading C args).
+    The code buffers are laid out for n_cap tokens (0: n)."""
     torch = _torch()
     _need(q, "q")
     B, Hq, d = q.shape
@@ -202,8 +204,9 @@ def _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
     Hkv = k_scale.shape[1]
     T = 0 if k_tail is None else k_tail.shape[2]
     if n > 0:
-        _need(k_codes, "k_codes", code_words_shape(B, Hkv, n, d, bits, CQ_LAYOUT_K), torch.int32, dev)
-        _need(v_codes, "v_codes", code_words_shape(B, Hkv, n, d, bits, CQ_LAYOUT_V), torch.int32, dev)
+        cap = n_cap or n
+        _need(k_codes, "k_codes", code_words_shape(B, Hkv, cap, d, bits, CQ_LAYOUT_K), torch.int32, dev)
+        _need(v_codes, "v_codes", code_words_shape(B, Hkv, cap, d, bits, CQ_LAYOUT_V), torch.int32, dev)
     for name, t in (("k_scale", k_scale), ("k_min", k_min), ("v_scale", v_scale), ("v_min", v_min)):
         _need(t, name, (B, Hkv, d), torch.float32, dev)
     tail_code = CQ_F16
@@ -222,16 +225,17 @@ def _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
 
 def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, *, n: int,
                    bits: int, sm_scale: float, calib=None, out=None, out_dtype=None, workspace=None,
-                   path: int = CQ_PATH_AUTO, splits: int = 0):
-    """One decode step; q [B, Hq, d]; codes/params from cq_quantize_kv; tails [B, Hkv, T, d] or None."""
+                   path: int = CQ_PATH_AUTO, splits: int = 0, n_cap: int = 0):
+    """One decode step; q [B, Hq, d]; codes/params from cq_quantize_kv; tails [B, Hkv, T, d] or None.
+    n_cap > n: the code buffers are laid out for n_cap tokens, of which the first n are attended over."""
     torch = _torch()
     B, Hq, Hkv, T, d, out, lead = _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
-                                                  v_tail, n, bits, out, out_dtype)
+                                                  v_tail, n, bits, out, out_dtype, n_cap)
     ws_bytes = lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, bits)
     if workspace is None and ws_bytes:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
     c = make_calib(calib)
-    opts = cq_opts(path, splits, 0)
+    opts = cq_opts(path, splits, 0, n_cap)
     st = lib.cq_decode_attn(*lead, float(sm_scale), None if c is None else ctypes.byref(c), _ptr(out),
                             _dtype_code(out), _ptr(workspace), 0 if workspace is None else workspace.numel(),
                             ctypes.byref(opts), _stream(q.device))
@@ -241,13 +245,13 @@ def cq_decode_attn(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, 
 
 def cq_decode_attn_noalloc(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail, v_tail, *, n: int,
                            bits: int, sm_scale: float, out, calib=None, path: int = CQ_PATH_AUTO,
-                           splits: int = 0):
+                           splits: int = 0, n_cap: int = 0):
     """cq_decode_attn into a caller's `out` with the library's fixed device
     scratch: no device memory is allocated, here or in the library."""
     _, _, _, _, _, out, lead = _decode_marshal(q, k_codes, k_scale, k_min, v_codes, v_scale, v_min, k_tail,
-                                               v_tail, n, bits, out, None)
+                                               v_tail, n, bits, out, None, n_cap)
     c = make_calib(calib)
-    opts = cq_opts(path, splits, 0)
+    opts = cq_opts(path, splits, 0, n_cap)
     st = lib.cq_decode_attn_noalloc(*lead, float(sm_scale), None if c is None else ctypes.byref(c), _ptr(out),
                                     _dtype_code(out), ctypes.byref(opts), _stream(q.device))
     _check(st, "cq_decode_attn_noalloc")

@@ -40,17 +40,20 @@ class QuantizedVisualKV:
         if k_visual.shape != v_visual.shape:
             raise ValueError(f"K {tuple(k_visual.shape)} and V {tuple(v_visual.shape)} differ")
         self.B, self.Hkv, self.n, self.d = k_visual.shape
+        self.n_cap = self.n
         # each (codes, scale, min); check=True synchronizes once and raises if a
         # workgroup of the fused quantizer gave up waiting (invalid codes)
         self.k, self.v = cq_quantize_kv_pair(k_visual, v_visual, bits, check=True)
 
     @classmethod
-    def from_codes(cls, k, v, n: int, bits: int) -> "QuantizedVisualKV":
+    def from_codes(cls, k, v, n: int, bits: int, n_cap: int = 0) -> "QuantizedVisualKV":
         """Wrap codes made elsewhere (e.g. by a chunked prefill): k and v are
-        (codes, scale, min) in the K and V layouts for n tokens."""
+        (codes, scale, min) in the K and V layouts for n_cap tokens (0: n), of
+        which the first n are the segment."""
         self = cls(None, None, bits)
         self.B, self.Hkv, self.d = k[1].shape
         self.n = n
+        self.n_cap = n_cap or n
         self.k, self.v = tuple(k), tuple(v)
         return self
 
@@ -88,7 +91,7 @@ class CalibQuantAttention(torch.nn.Module):
         T = 0 if k_tail is None else k_tail.shape[2]
         return cq_decode_attn(q, *cache.k, *cache.v, k_tail, v_tail, n=cache.n, bits=cache.bits,
                               sm_scale=self.sm_scale, calib=self.calib, out=out,
-                              workspace=self._workspace(q, cache, T))
+                              workspace=self._workspace(q, cache, T), n_cap=cache.n_cap)
 
 
 class GraphedDecode:

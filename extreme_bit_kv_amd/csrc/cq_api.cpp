@@ -77,7 +77,7 @@ cq_status cq_quantize_kv(const void* x, cq_dtype x_dtype, int32_t B, int32_t H, 
     return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_WIDE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (scale == nullptr || minv == nullptr) return CQ_ERR_INVALID_ARG;
@@ -111,7 +111,7 @@ cq_status cq_quantize_kv_pair(const void* k, const void* v, cq_dtype x_dtype, in
   if (!fits(B, H, n, d) || d <= 0 || !valid_bits(bits) || !valid_dtype(x_dtype)) return CQ_ERR_INVALID_ARG;
   if ((d * bits) % 32 != 0) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_WIDE || opt_polls(opts) < 0) return CQ_ERR_INVALID_ARG;
   const int64_t units = (int64_t)B * H;
   if (units > 0) {
     if (k_scale == nullptr || k_min == nullptr || v_scale == nullptr || v_min == nullptr) return CQ_ERR_INVALID_ARG;
@@ -228,7 +228,10 @@ cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes,
   if ((d * bits) % 32 != 0 || n + (int64_t)T < 1) return CQ_ERR_INVALID_ARG;
   if (!(sm_scale == sm_scale)) return CQ_ERR_INVALID_ARG;
   const int path = opt_path(opts);
-  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_PIPE || (opts && opts->splits < 0)) return CQ_ERR_INVALID_ARG;
+  if (path < CQ_PATH_AUTO || path > CQ_PATH_FAST_WIDE || (opts && opts->splits < 0)) return CQ_ERR_INVALID_ARG;
+  // token capacity of the code buffers: the first n of n_cap tokens are attended over
+  const int32_t n_cap = opts && opts->n_cap != 0 ? opts->n_cap : n;
+  if (n_cap < n || !fits(B, Hkv, n_cap, d) || (n_cap != n && n_cap % 32 != 0)) return CQ_ERR_INVALID_ARG;
   if (B > 0) {
     if (q == nullptr || out == nullptr) return CQ_ERR_INVALID_ARG;
     if (n > 0 && (k_codes == nullptr || k_scale == nullptr || k_min == nullptr || v_codes == nullptr ||
@@ -247,7 +250,7 @@ cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes,
   a.k_codes = k_codes; a.k_scale = k_scale; a.k_min = k_min;
   a.v_codes = v_codes; a.v_scale = v_scale; a.v_min = v_min;
   a.k_tail = k_tail; a.v_tail = v_tail; a.tail_dtype = tail_dtype;
-  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.T = T; a.d = d; a.bits = bits;
+  a.B = B; a.Hq = Hq; a.Hkv = Hkv; a.n = n; a.T = T; a.d = d; a.bits = bits; a.nc = n_cap;
   a.sm_scale = sm_scale;
   a.calib_on = (calib != nullptr && calib->enabled) ? 1 : 0;
   if (a.calib_on) { a.a_lo = calib->a_lo; a.c_lo = calib->c_lo; a.a_hi = calib->a_hi; a.c_hi = calib->c_hi; }
@@ -258,8 +261,11 @@ cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes,
   const bool one_ok = cqi::decode_fast_supported(a);
   const bool split_ok = cqi::decode_split_supported(a);
   const bool pipe_ok = cqi::decode_pipe_supported(a);
-  enum { kGeneric, kOne, kSplit, kLds, kPipe } use = kGeneric;
-  if (path == CQ_PATH_FAST_LDS) {
+  enum { kGeneric, kOne, kSplit, kLds, kPipe, kWide } use = kGeneric;
+  if (path == CQ_PATH_FAST_WIDE) {
+    if (!cqi::decode_wide_supported(a)) return CQ_ERR_UNSUPPORTED;
+    use = kWide;
+  } else if (path == CQ_PATH_FAST_LDS) {
     if (!cqi::decode_lds_supported(a)) return CQ_ERR_UNSUPPORTED;
     use = kLds;
   } else if (path == CQ_PATH_FAST_PIPE) {
@@ -272,14 +278,15 @@ cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes,
     if (!split_ok) return CQ_ERR_UNSUPPORTED;
     use = kSplit;
   } else if (path == CQ_PATH_FAST || (path == CQ_PATH_AUTO && !(opts && opts->splits > 0))) {
-    if (cqi::decode_lds_preferred(a)) use = kLds;
+    if (cqi::decode_wide_preferred(a)) use = kWide;
+    else if (cqi::decode_lds_preferred(a)) use = kLds;
     else if (cqi::decode_split_preferred(a, one_ok)) use = kSplit;
     else if (one_ok) use = kOne;
     else if (path == CQ_PATH_FAST) return CQ_ERR_UNSUPPORTED;
   }
   const int req = use == kSplit && path == CQ_PATH_FAST_SPLIT ? a.splits : 0;
   size_t need;
-  if (use == kPipe) need = 0;
+  if (use == kPipe || use == kWide) need = 0;
   else if (use == kOne || use == kLds) need = cqi::decode_fast_ws(B, Hq, Hkv, n, T, d);
   else if (use == kSplit) need = cqi::decode_split_ws(B, Hkv, n, T, req);
   else need = cqi::decode_generic_ws(B, Hq, Hkv, n, T, d, cqi::decode_generic_splits(n, B * Hkv, a.splits));
@@ -297,6 +304,7 @@ cq_status decode_entry(const void* q, cq_dtype q_dtype, const uint32_t* k_codes,
   }
   clear_stale_hip_error();
   if (use == kPipe) return from_hip(cqi::decode_pipe(a));
+  if (use == kWide) return from_hip(cqi::decode_wide(a));
   if (use == kLds) return from_hip(cqi::decode_lds(a));
   if (use == kOne) return from_hip(cqi::decode_fast(a));
   if (use == kSplit) return from_hip(cqi::decode_split(a, req));

@@ -76,6 +76,7 @@ struct DecodeArgs {
   const void* v_tail;
   int tail_dtype;
   int B, Hq, Hkv, n, T, d, bits;
+  int nc;               // token capacity of the code buffers (>= n; their layout is that of nc tokens)
   float sm_scale;
   int calib_on;
   float a_lo, c_lo, a_hi, c_hi;
@@ -99,6 +100,12 @@ hipError_t decode_pipe(const DecodeArgs& a);
 // device address on the current device (resolved once per device).
 constexpr size_t kScratchBytes = (size_t)16 << 20;
 hipError_t scratch_address(void** out);
+
+// b = 1, every code tile of a unit in flight at once (n <= 8192, T <= 256;
+// one 8-wave workgroup per unit, at most one unit per CU)
+bool decode_wide_supported(const DecodeArgs& a);
+bool decode_wide_preferred(const DecodeArgs& a);   // the automatic choice
+hipError_t decode_wide(const DecodeArgs& a);
 
 // b = 1, visual scores kept in LDS (one 16-wave workgroup per CU walking its units)
 bool decode_lds_supported(const DecodeArgs& a);

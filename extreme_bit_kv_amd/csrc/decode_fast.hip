@@ -131,6 +131,7 @@ struct Params {
   float sm;
   int calib_on;
   float a_lo, c_lo, a_hi, c_hi;
+  int nc;               // token capacity of the code buffers (their layout is that of nc >= n tokens)
 };
 
 // A text tail longer than the fused pass takes (T > kMaxTail), for one unit,
@@ -273,8 +274,15 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
 // them in one dtype.
 // LT: the text tail is longer than kMaxTail (a separate instance, so that the
 // chunked tail's registers do not weigh on the kernel of the common case)
-template <int G, bool F32, bool LT>
-__global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
+// TPW > 0: every code tile of the unit in flight at once, for launches of at
+// most one workgroup per CU.  Wave w owns tiles w, w + 8, ... (at most TPW);
+// its key and value tiles, and the text tail, are all requested at the start,
+// and the scores stay in registers between the two passes (no second read of
+// the keys).  The arithmetic is the same as with dealt tiles (min / max and
+// exact integer sums do not depend on which wave took a tile), so the outputs
+// are the same bit for bit.  Two waves per SIMD: up to 256 VGPRs.
+template <int G, bool F32, bool LT, int TPW = 0>
+__global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   const int unit = blockIdx.x;
   const int b = unit / P.Hkv, h = unit % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -284,6 +292,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   const int Tf = LT ? 0 : T;
   const int ntiles = (n + kTile - 1) / kTile;
   const int R = n >> 5;
+  const int nc = P.nc, Rc = nc >> 5;           // the code buffers' layout: nc tokens
   // Issue priority: the two workgroups on a CU would otherwise run their key
   // passes unevenly (the older one first), leaving the other's value pass
   // alone at the end.  High through the key pass (latency-bound), low through
@@ -330,9 +339,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   // Code tiles are read with buffer loads: one descriptor per unit and tensor,
   // a fixed byte offset per lane plus the tile's (wave-uniform); a tile past
   // the last reads out of range, which returns zeros without any traffic.
-  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (n > 0 ? (size_t)unit * 4 * n : 0)), (short)0,
-                                                    n * 16, kRsrcFlags);
-  const uint32_t koff = (uint32_t)(g4 * n + 8 * i16) * 4u;
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (n > 0 ? (size_t)unit * 4 * nc : 0)), (short)0,
+                                                    n > 0 ? nc * 16 : 0, kRsrcFlags);
+  const uint32_t koff = (uint32_t)(g4 * nc + 8 * i16) * 4u;
   auto load_k = [&](int tile, uint4& w0, uint4& w1) {   // tokens past n: scores not used
     const uint32_t off = koff + (tile < ntiles ? (uint32_t)tile * 512u : 0x80000000u);
     w0 = ld_buf(rk, off);
@@ -359,11 +368,51 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       ktp[r][1] = make_uint4(0, 0, 0, 0);
     }
   }
+  // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
+  // tokens whose p is 0: whatever codes they read, their digits are 0.
+  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vcb + (n > 0 ? (size_t)unit * Rc * 128 : 0)), (short)0,
+                                                    R * 512, kRsrcFlags);
+  const uint32_t voff = (uint32_t)(g4 * 128 + 8 * i16) * 4u;
+  auto load_v = [&](int tile, uint4& w0, uint4& w1) {
+    const uint32_t off = voff + (tile < ntiles ? (uint32_t)tile * 2048u : 0x80000000u);
+    w0 = ld_buf(rv, off);
+    w1 = ld_buf(rv, off + 16u);
+  };
+  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
+  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
+  constexpr int kPhases = kThreads / 64;
+  const int vcp = tid & 63, vph = tid >> 6;
+  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
+  auto load_vtail = [&]() {
+#pragma unroll
+    for (int i = 0; i < kPreTail / kPhases; ++i) {
+      const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
+      if constexpr (F32) {
+        const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+        vtr[i][0] = x.x;
+        vtr[i][F32 ? 1 : 0] = x.y;
+      } else {
+        vtr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
+      }
+    }
+  };
   // the key pass keeps two tiles of look-ahead per wave (kn, km), the value
-  // pass one (kn, vn); the first two are requested under the prologue
+  // pass one (kn, vn); the first two are requested under the prologue.  With
+  // TPW > 0 every tile of the wave is requested here: keys, the tail values,
+  // then values (the order in which they are used).
   uint4 kn0, kn1, km0, km1;
-  load_k(wave, kn0, kn1);
-  load_k(wave + kWaves, km0, km1);
+  constexpr int kSlots = TPW > 0 ? TPW : 1;
+  uint4 kwide[kSlots][2], vwide[kSlots][2];
+  if constexpr (TPW > 0) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) load_k(wave + kWaves * k, kwide[k][0], kwide[k][1]);
+    load_vtail();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) load_v(wave + kWaves * k, vwide[k][0], vwide[k][1]);
+  } else {
+    load_k(wave, kn0, kn1);
+    load_k(wave + kWaves, km0, km1);
+  }
   // Tiles are dealt dynamically: wave w starts with tile w and then takes the
   // next untaken one, so that a wave whose loads come back late does not hold
   // up the workgroup at the next barrier.  (Results do not depend on which
@@ -534,9 +583,24 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
     }
   };
   float vmin = INFINITY, vmax = -INFINITY;
+  float swide[kSlots][8];                       // TPW > 0: the wave's scores, kept for the value pass
+  if constexpr (TPW > 0) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + kWaves * k;
+      if (tile < ntiles) {
+        scores(kwide[k][0], kwide[k][1], swide[k]);
+        const float* st = swide[k];
+        if ((tile + 1) * kTile <= n || tile * kTile + 8 * i16 < n) {
+          vmin = min3f(min3f(vmin, st[0], st[1]), min3f(st[2], st[3], st[4]), min3f(st[5], st[6], st[7]));
+          vmax = max3f(max3f(vmax, st[0], st[1]), max3f(st[2], st[3], st[4]), max3f(st[5], st[6], st[7]));
+        }
+      }
+    }
+  }
   // a wave's tiles come in increasing order: tile, then tnext (loading into
   // km), then nxt
-  for (int tile = wave, tnext = wave + kWaves; tile < ntiles;) {
+  for (int tile = wave, tnext = wave + kWaves; TPW == 0 && tile < ntiles;) {
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&s_next[0], 1);
     nxt = __builtin_amdgcn_readfirstlane(nxt);
@@ -563,34 +627,11 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   // the second pass's loads equal the first's and keeps every first-pass score
   // alive instead of recomputing it.)
   asm("" : "+s"(kc));
-  load_k(wave, kn0, kn1);
-  // V word row of this lane, channels 8*i16 .. +7.  Rows past the last hold
-  // tokens whose p is 0: whatever codes they read, their digits are 0.
-  const auto rv = __builtin_amdgcn_make_buffer_rsrc((void*)(vcb + (n > 0 ? (size_t)unit * R * 128 : 0)), (short)0,
-                                                    R * 512, kRsrcFlags);
-  const uint32_t voff = (uint32_t)(g4 * 128 + 8 * i16) * 4u;
-  auto load_v = [&](int tile, uint4& w0, uint4& w1) {
-    const uint32_t off = voff + (tile < ntiles ? (uint32_t)tile * 2048u : 0x80000000u);
-    w0 = ld_buf(rv, off);
-    w1 = ld_buf(rv, off + 16u);
-  };
   uint4 vn0, vn1;
-  load_v(wave, vn0, vn1);
-  // tail values: thread (channel pair vcp, phase vph) holds channels 2 vcp,
-  // 2 vcp + 1 of tokens vph + kPhases i, as raw bits converted where used
-  constexpr int kPhases = kThreads / 64;
-  const int vcp = tid & 63, vph = tid >> 6;
-  uint32_t vtr[kPreTail / kPhases][F32 ? 2 : 1];
-#pragma unroll
-  for (int i = 0; i < kPreTail / kPhases; ++i) {
-    const size_t e = ((size_t)unit * T + max(min(vph + kPhases * i, T - 1), 0)) * 128 + 2 * vcp;
-    if constexpr (F32) {
-      const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
-      vtr[i][0] = x.x;
-      vtr[i][F32 ? 1 : 0] = x.y;
-    } else {
-      vtr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
-    }
+  if constexpr (TPW == 0) {
+    load_k(wave, kn0, kn1);
+    load_v(wave, vn0, vn1);
+    load_vtail();
   }
   // ---- min / max of every head's visual scores ---------------------------
 #pragma unroll
@@ -718,20 +759,14 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
   int wtiles = 0;
   double psum = 0.0;                            // sum of this lane's P (exact: integers below 2^53)
   unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
-  for (int tile = wave; tile < ntiles;) {
-    int nxt = 0;
-    if (lane == 0) nxt = atomicAdd(&s_next[1], 1);
-    nxt = __builtin_amdgcn_readfirstlane(nxt);
-    const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
-    load_k(nxt, kn0, kn1);
-    load_v(nxt, vn0, vn1);
-    // probabilities of this lane's 8 tokens (head oh), relative to the
-    // largest calibrated visual score, as fixed point P = round(p 2^27);
-    // tokens that do not count get exponent -inf, so p = 0
+  // one value tile: probabilities of this lane's 8 tokens (head oh),
+  // relative to the largest calibrated visual score, as fixed point
+  // P = round(p 2^27) (tokens that do not count get exponent -inf, so p = 0),
+  // their digits through LDS to the A lanes, the products with the V words
+  auto value_tile = [&](int tile, const float (&st)[8], const uint4& vw0, const uint4& vw1)
+                        __attribute__((always_inline)) {
     const bool ok = oh < G && tile * kTile + 8 * i16 < n;
     const float mu_t = ok ? mu2 : -INFINITY;
-    float st[8];
-    scores(kw0, kw1, st);
     uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
@@ -764,6 +799,24 @@ __global__ void __launch_bounds__(kThreads, 4) df_b1(Params P) {
       vacc[ct] = mfma(av1, bits_hi(vwd[ct]), vacc[ct]);
     }
     wave_sync_lds();                       // digits read before the next tile overwrites them
+  };
+  if constexpr (TPW > 0) {
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) {
+      const int tile = wave + kWaves * k;
+      if (tile < ntiles) value_tile(tile, swide[k], vwide[k][0], vwide[k][1]);
+    }
+  }
+  for (int tile = wave; TPW == 0 && tile < ntiles;) {
+    int nxt = 0;
+    if (lane == 0) nxt = atomicAdd(&s_next[1], 1);
+    nxt = __builtin_amdgcn_readfirstlane(nxt);
+    const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
+    load_k(nxt, kn0, kn1);
+    load_v(nxt, vn0, vn1);
+    float st[8];
+    scores(kw0, kw1, st);
+    value_tile(tile, st, vw0, vw1);
     if (++wtiles == kFlushTiles) {
       flush();
       wtiles = 0;
@@ -841,6 +894,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
   const int n = P.n, T = P.T;
   const int ntiles = (n + kTile - 1) / kTile;
   const int R = n >> 5;
+  const int nc = P.nc, Rc = nc >> 5;           // the code buffers' layout: nc tokens
   constexpr int kRegion = G * 128;            // words per tile: G x 128 scores, then G x 4 x 128 digit bytes
 
   __shared__ float s_q[4][128];
@@ -874,13 +928,13 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
   // of being hoisted out of the loop (and spilled).
   auto load_k = [&](int u, int tile, int t, uint4& w0, uint4& w1) {   // tokens past n: scores not used
     const int tok = max(min(tile * kTile + 8 * (t & 15), n - 8), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)u * 4 + ((t & 63) >> 4)) * n + tok);
+    const uint4* src = reinterpret_cast<const uint4*>(kc + ((size_t)u * 4 + ((t & 63) >> 4)) * nc + tok);
     w0 = src[0];
     w1 = src[1];
   };
   auto load_v = [&](int u, int tile, int t, uint4& w0, uint4& w1) {
     const int row = max(min(tile * 4 + ((t & 63) >> 4), R - 1), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)u * R + row) * 128 + 8 * (t & 15));
+    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)u * Rc + row) * 128 + 8 * (t & 15));
     w0 = src[0];
     w1 = src[1];
   };
@@ -1382,6 +1436,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   const int Tf = LT ? 0 : T;                   // the text tail in the fused pass (else chunked at the end)
   const int tiles = (n + TB - 1) / TB;
   const int R = n / E;
+  const int nc = P.nc, Rc = nc / E;            // the code buffers' layout: nc tokens
 
   __shared__ float s_q[4][128];
   __shared__ float s_qp[4][128];
@@ -1412,7 +1467,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     {
 #pragma unroll
       for (int p = 0; p < BITS; ++p) {
-        const uint32_t* src = kc + ((size_t)unit * W + BITS * g4 + p) * n + tok0;
+        const uint32_t* src = kc + ((size_t)unit * W + BITS * g4 + p) * nc + tok0;
         if constexpr (TPL == 4) {
           const uint4 x = *reinterpret_cast<const uint4*>(src);
           w[4 * p] = x.x; w[4 * p + 1] = x.y; w[4 * p + 2] = x.z; w[4 * p + 3] = x.w;
@@ -1562,7 +1617,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   load_k(wave, kn);
   auto load_v = [&](int tile, uint32_t (&w)[8]) {   // rows past the last: p = 0 (as in df_b1)
     const int row = max(min(tile * 4 + g4, R - 1), 0);
-    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * R + row) * 128 + 8 * i16);
+    const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * Rc + row) * 128 + 8 * i16);
     const uint4 x0 = src[0], x1 = src[1];
     w[0] = x0.x; w[1] = x0.y; w[2] = x0.z; w[3] = x0.w;
     w[4] = x1.x; w[5] = x1.y; w[6] = x1.z; w[7] = x1.w;
@@ -1854,6 +1909,39 @@ hipError_t launch_f(const Params& p, int G, int units, hipStream_t st) {
   return p.T > kMaxTail ? launch_f1<F32, true>(p, G, units, st) : launch_f1<F32, false>(p, G, units, st);
 }
 
+template <bool F32, int TPW>
+hipError_t launch_w1(const Params& p, int G, int units, hipStream_t st) {
+  if (G == 1) { CQ_LAUNCH((df_b1<1, F32, false, TPW>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_b1<2, F32, false, TPW>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_b1<4, F32, false, TPW>), dim3(units), dim3(kThreads), 0, st, p);
+  return hipSuccess;
+}
+
+// tiles per wave of the all-in-flight instance: 2 or 4 (n <= 4096; with 8,
+// the key, score and value registers of a wave exceed its 256 VGPRs)
+constexpr int kWideTiles = 4;
+int wide_tpw(int n) {
+  const int per_wave = ((n + kTile - 1) / kTile + kWaves - 1) / kWaves;
+  return per_wave <= 2 ? 2 : 4;
+}
+
+template <bool F32>
+hipError_t launch_w(const Params& p, int G, int units, hipStream_t st) {
+  if (wide_tpw(p.n) == 2) return launch_w1<F32, 2>(p, G, units, st);
+  return launch_w1<F32, 4>(p, G, units, st);
+}
+
+// CUs of the current device (0 if unknown)
+long device_cus() {
+  static long cache[64];
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cache[dev] > 0) return cache[dev];
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  cache[dev] = cus;
+  return cache[dev];
+}
+
 // Co-resident workgroups of an LDS-score kernel on the current device.
 long lds_capacity(const void* fn, int slot) {
   static long cache[64][6];
@@ -1915,6 +2003,31 @@ bool decode_fast_supported(const DecodeArgs& a) {
          (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && (a.T == 0 || a.tail_dtype == a.q_dtype);
 }
 
+bool decode_wide_supported(const DecodeArgs& a) {
+  const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
+  return a.bits == 1 && a.d == 128 && (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && a.n <= kWaves * kWideTiles * kTile &&
+         a.T <= kMaxTail && (a.T == 0 || a.tail_dtype == a.q_dtype);
+}
+
+// The all-in-flight instance needs a CU of its own per (batch, kv head)
+// unit: its workgroups hold half of a CU's registers, and with more units
+// than CUs the second round of workgroups would start only after the first.
+bool decode_wide_preferred(const DecodeArgs& a) {
+  if (!decode_wide_supported(a)) return false;
+  const long cus = device_cus();
+  return cus > 0 && (long)a.B * a.Hkv <= cus;
+}
+
+hipError_t decode_wide(const DecodeArgs& a) {
+  const int units = a.B * a.Hkv;
+  if (units == 0) return hipSuccess;
+  Params p{a.q, a.k_codes, a.k_scale, a.k_min, a.v_codes, a.v_scale, a.v_min, a.k_tail, a.v_tail, a.out,
+           a.Hq, a.Hkv, a.n, a.T, a.q_dtype == CQ_F32, a.tail_dtype == CQ_F32, a.out_dtype == CQ_F32,
+           a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi, a.nc};
+  const int G = a.Hq / a.Hkv;
+  return a.q_dtype == CQ_F32 ? launch_w<true>(p, G, units, a.stream) : launch_w<false>(p, G, units, a.stream);
+}
+
 bool decode_lds_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
   return a.bits == 1 && a.d == 128 && (G == 1 || G == 2 || G == 4) && a.n % 32 == 0 && a.T <= kMaxTail &&
@@ -1938,7 +2051,7 @@ hipError_t decode_lds(const DecodeArgs& a) {
   if (units == 0) return hipSuccess;
   Params p{a.q, a.k_codes, a.k_scale, a.k_min, a.v_codes, a.v_scale, a.v_min, a.k_tail, a.v_tail, a.out,
            a.Hq, a.Hkv, a.n, a.T, a.q_dtype == CQ_F32, a.tail_dtype == CQ_F32, a.out_dtype == CQ_F32,
-           a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi};
+           a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi, a.nc};
   const int G = a.Hq / a.Hkv;
   return a.q_dtype == CQ_F32 ? launch_l<true>(p, G, units, a.stream) : launch_l<false>(p, G, units, a.stream);
 }
@@ -1948,7 +2061,7 @@ hipError_t decode_fast(const DecodeArgs& a) {
   if (units == 0) return hipSuccess;
   Params p{a.q, a.k_codes, a.k_scale, a.k_min, a.v_codes, a.v_scale, a.v_min, a.k_tail, a.v_tail, a.out,
            a.Hq, a.Hkv, a.n, a.T, a.q_dtype == CQ_F32, a.tail_dtype == CQ_F32, a.out_dtype == CQ_F32,
-           a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi};
+           a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi, a.c_hi, a.nc};
   const int G = a.Hq / a.Hkv;
   if (a.bits > 1)
     return a.q_dtype == CQ_F32 ? launch_b<true>(p, a.bits, G, units, a.stream)

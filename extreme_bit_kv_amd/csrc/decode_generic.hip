@@ -25,6 +25,7 @@ constexpr int kMaxSplits = 64;
 
 struct Shape {
   int B, Hq, Hkv, G, n, T, d, bits, S;
+  int nc;    // token capacity of the code buffers (their layout is that of nc >= n tokens)
 };
 
 __device__ __forceinline__ void split_range(int n, int S, int s, int& t0, int& t1) {
@@ -71,7 +72,7 @@ __global__ void __launch_bounds__(kThreads) dg_scores(Shape sh, const QT* __rest
 #pragma unroll
     for (int g = 0; g < kGMax; ++g) acc[g] = 0.f;
     for (int w = 0; w < W; ++w) {
-      uint32_t word = kc[((size_t)unit * W + w) * sh.n + i];
+      uint32_t word = kc[((size_t)unit * W + w) * sh.nc + i];
       for (int e = 0; e < E; ++e) {
         float c = (float)((word >> cqd::code_off(e, sh.bits)) & L);
         int j = w * E + e;
@@ -160,7 +161,7 @@ __global__ void __launch_bounds__(kThreads) dg_attend(Shape sh, CalibP cal, cons
     __syncthreads();
     int t0, t1;
     split_range(sh.n, sh.S, split, t0, t1);
-    const int E = 32 / sh.bits, L = (1 << sh.bits) - 1, R = (sh.n + E - 1) / E;
+    const int E = 32 / sh.bits, L = (1 << sh.bits) - 1, R = (sh.nc + E - 1) / E;   // word rows per unit
     const int pg = threadIdx.x / 32, pe = threadIdx.x % 32;     // (head, element) of the p producer
     for (int r = t0 / E; r * E < t1; ++r) {
       if (pg < G && pe < E) {
@@ -274,7 +275,7 @@ __global__ void dg_merge(Shape sh, const float* __restrict__ part, const float* 
 
 template <typename QT, typename TT, typename OT>
 hipError_t run(const cqi::DecodeArgs& a, int S) {
-  Shape sh{a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.n, a.T, a.d, a.bits, S};
+  Shape sh{a.B, a.Hq, a.Hkv, a.Hq / a.Hkv, a.n, a.T, a.d, a.bits, S, a.nc};
   const int units = a.B * a.Hkv;
   if (units == 0) return hipSuccess;
   const int nsplit = S + (a.T > 0 ? 1 : 0);
@@ -341,7 +342,7 @@ hipError_t visual_scores(const void* q, int q_dtype, const uint32_t* k_codes, co
   const int units = B * Hkv;
   if (units == 0 || n == 0) return hipSuccess;
   const int S = decode_generic_splits(n, units, 0);
-  Shape sh{B, Hq, Hkv, Hq / Hkv, n, 0, kD, bits, S};
+  Shape sh{B, Hq, Hkv, Hq / Hkv, n, 0, kD, bits, S, n};
   if (q_dtype == CQ_F16)
     CQ_LAUNCH(dg_scores<__half>, dim3(S, units), dim3(kThreads), 0, st, sh, (const __half*)q, k_codes, k_scale,
               k_min, sm_scale, scores, (float2*)nullptr);

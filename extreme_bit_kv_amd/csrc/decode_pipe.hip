@@ -80,6 +80,7 @@ struct PP {
   const void* vt;
   void* out;
   int Hq, Hkv, n, T, units;
+  int nc;               // token capacity of the code buffers (their layout is that of nc >= n tokens)
   int out_f32;
   float sm;
   int calib_on;
@@ -160,9 +161,9 @@ __global__ void __launch_bounds__(KW * 64, 1) dp_b1(PP P) {
   // of tile t inside a unit's codes.  Keys [4 word rows][n tokens]: the lane
   // reads tokens 4 i16 .. +3 and 64 + 4 i16 .. +3 of word row g4.  Values
   // [n / 32 rows][128 channels]: row 4 t + g4, channels 4 i16 .. +3 and 64 + ...
-  const uint32_t koff = (uint32_t)(g4 * n + 4 * i16) * 4u;
+  const uint32_t koff = (uint32_t)(g4 * P.nc + 4 * i16) * 4u;
   const uint32_t voff = (uint32_t)(g4 * 128 + 4 * i16) * 4u;
-  const uint32_t kbytes = (uint32_t)n * 16u, vbytes = (uint32_t)R * 512u;
+  const uint32_t kbytes = (uint32_t)P.nc * 16u, vbytes = (uint32_t)(P.nc >> 5) * 512u;   // per unit
   // key tile k / value tile k of unit j (wave-uniform).  One descriptor per
   // code tensor (each at most 2 GB); the tile's byte offset (unit and tile:
   // wave-uniform) joins the lane's; a tile past the unit or a unit past the
@@ -813,7 +814,7 @@ bool decode_pipe_supported(const DecodeArgs& a) {
   const int G = a.Hkv > 0 ? a.Hq / a.Hkv : 0;
   return a.bits == 1 && a.d == 128 && (G == 1 || G == 2 || G == 4) && a.n >= 32 &&
          a.n <= kMaxTiles * kTile && a.n % 32 == 0 && a.T <= kMaxT && (a.T == 0 || a.tail_dtype == a.q_dtype) &&
-         (long)a.B * a.Hkv >= 1 && (long long)a.B * a.Hkv * a.n * 16 <= (1ll << 31);
+         (long)a.B * a.Hkv >= 1 && (long long)a.B * a.Hkv * a.nc * 16 <= (1ll << 31);
 }
 
 hipError_t decode_pipe(const DecodeArgs& a) {
@@ -835,6 +836,7 @@ hipError_t decode_pipe(const DecodeArgs& a) {
   p.Hq = a.Hq;
   p.Hkv = a.Hkv;
   p.n = a.n;
+  p.nc = a.nc;
   p.T = a.T;
   p.units = units;
   p.out_f32 = a.out_dtype == CQ_F32;

@@ -71,6 +71,7 @@ struct SParams {
   float* tsc;          // [unit][4][T]: text-tail scores
   float* tmx;          // [unit][4]: their max
   float* part;         // [unit][nc + 1][4][kPart]: chunk records, then the tail record
+  int ncap;            // token capacity of the code buffers (their layout is that of ncap >= n tokens)
 };
 
 struct QSmem {
@@ -220,10 +221,10 @@ __device__ __forceinline__ void tile_scores(const KeyOp& k, const uint4& w0, con
 // Key words of this lane for a tile: plane g4 of tokens tile*128 + tok_of(i16, m).
 __device__ __forceinline__ int tok_of(int i16, int m) { return (m < 4 ? 4 * i16 : 64 + 4 * i16 - 4) + m; }
 
-__device__ __forceinline__ void load_key(const uint32_t* kc, int unit, int n, int tile, int lane, uint4& w0,
-                                         uint4& w1) {
+__device__ __forceinline__ void load_key(const uint32_t* kc, int unit, int n, int ncap, int tile, int lane,
+                                         uint4& w0, uint4& w1) {
   const int i16 = lane & 15, g4 = lane >> 4;
-  const uint32_t* plane = kc + ((size_t)unit * 4 + g4) * n;
+  const uint32_t* plane = kc + ((size_t)unit * 4 + g4) * ncap;
   w0 = *reinterpret_cast<const uint4*>(plane + min(tile * kTile + 4 * i16, n - 4));
   w1 = *reinterpret_cast<const uint4*>(plane + min(tile * kTile + 64 + 4 * i16, n - 4));
 }
@@ -232,10 +233,10 @@ __device__ __forceinline__ void load_key(const uint32_t* kc, int unit, int n, in
 // channels ch_of(i16, c), c < 8.
 __device__ __forceinline__ int ch_of(int i16, int c) { return (c < 4 ? 4 * i16 : 64 + 4 * i16 - 4) + c; }
 
-__device__ __forceinline__ void load_val(const uint32_t* vc, int unit, int R, int tile, int lane, uint4& w0,
-                                         uint4& w1) {
+__device__ __forceinline__ void load_val(const uint32_t* vc, int unit, int R, int Rcap, int tile, int lane,
+                                         uint4& w0, uint4& w1) {
   const int i16 = lane & 15, g4 = lane >> 4;
-  const uint32_t* row = vc + ((size_t)unit * R + min(tile * 4 + g4, R - 1)) * 128;
+  const uint32_t* row = vc + ((size_t)unit * Rcap + min(tile * 4 + g4, R - 1)) * 128;
   w0 = *reinterpret_cast<const uint4*>(row + 4 * i16);
   w1 = *reinterpret_cast<const uint4*>(row + 64 + 4 * i16);
 }
@@ -259,7 +260,7 @@ __global__ void __launch_bounds__(kThreads, 4) ds_keys(SParams P) {
   uint4 kw[D][2];
 #pragma unroll
   for (int t = 0; t < D; ++t)
-    load_key(P.kc, unit, n, chunk * P.ct + wave + kWaves * t, lane, kw[t][0], kw[t][1]);
+    load_key(P.kc, unit, n, P.ncap, chunk * P.ct + wave + kWaves * t, lane, kw[t][0], kw[t][1]);
   q_prologue<G, F32>(P, ql, qs);
   const KeyOp ko = key_op<G>(qs, lane);
 
@@ -272,7 +273,7 @@ __global__ void __launch_bounds__(kThreads, 4) ds_keys(SParams P) {
     const bool okB = tile < ntiles && tile * kTile + tok_of(i16, 4) < n;
     float st[8];
     const uint4 w0 = kw[t % D][0], w1 = kw[t % D][1];
-    if (t + D < MT) load_key(P.kc, unit, n, tile + kWaves * D, lane, kw[t % D][0], kw[t % D][1]);
+    if (t + D < MT) load_key(P.kc, unit, n, P.ncap, tile + kWaves * D, lane, kw[t % D][0], kw[t % D][1]);
     tile_scores(ko, w0, w1, st);
     const float amin = fminf(fminf(st[0], st[1]), fminf(st[2], st[3]));
     const float amax = fmaxf(fmaxf(st[0], st[1]), fmaxf(st[2], st[3]));
@@ -394,8 +395,8 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
   const float tmx0 = P.tmx[(size_t)unit * 4 + hw];
   const int tile0 = chunk * P.ct + wave;
   uint4 kn0, kn1, vn0, vn1;                    // one tile of look-ahead
-  load_key(P.kc, unit, n, tile0, lane, kn0, kn1);
-  load_val(P.vc, unit, R, tile0, lane, vn0, vn1);
+  load_key(P.kc, unit, n, P.ncap, tile0, lane, kn0, kn1);
+  load_val(P.vc, unit, R, P.ncap >> 5, tile0, lane, vn0, vn1);
   q_prologue<G, F32>(P, ql, qs);
   const KeyOp ko = key_op<G>(qs, lane);
 
@@ -445,8 +446,8 @@ __global__ void __launch_bounds__(kThreads, 4) ds_vals(SParams P) {
     if (tile >= ntiles) break;
     const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
     if (t + 1 < MT) {
-      load_key(P.kc, unit, n, tile + kWaves, lane, kn0, kn1);
-      load_val(P.vc, unit, R, tile + kWaves, lane, vn0, vn1);
+      load_key(P.kc, unit, n, P.ncap, tile + kWaves, lane, kn0, kn1);
+      load_val(P.vc, unit, R, P.ncap >> 5, tile + kWaves, lane, vn0, vn1);
     }
     // probabilities of this lane's 8 tokens (head oh), as 22-bit fixed point
     const bool okA = oh < G && tile * kTile + tok_of(i16, 0) < n;
@@ -682,7 +683,7 @@ hipError_t decode_split(const DecodeArgs& a, int requested) {
   SParams p{a.q, a.k_codes, a.k_scale, a.k_min, a.v_codes, a.v_scale, a.v_min, a.k_tail, a.v_tail, a.out,
             a.Hq, a.Hkv, a.n, a.T, a.out_dtype == CQ_F32, a.sm_scale, a.calib_on, a.a_lo, a.c_lo, a.a_hi,
             a.c_hi, c.nc, c.ct, reinterpret_cast<float*>(ws + w.mm), reinterpret_cast<float*>(ws + w.tsc),
-            reinterpret_cast<float*>(ws + w.tmx), reinterpret_cast<float*>(ws + w.part)};
+            reinterpret_cast<float*>(ws + w.tmx), reinterpret_cast<float*>(ws + w.part), a.nc};
   const int G = a.Hq / a.Hkv;
   return a.q_dtype == CQ_F32 ? launch_f<true>(p, G, c.mt, units, a.stream)
                              : launch_f<false>(p, G, c.mt, units, a.stream);

@@ -19,9 +19,11 @@ written, and the codes of the complete segment equal the one-shot codes.
 With ``eager=True`` each ``append`` also codes the new rows on the range known
 so far and codes again the earlier rows of every (batch, head) whose range
 the new rows widened, so the codes are those of the segment so far after
-every call.  Ranges keep widening while the segment is short, so this
-re-reads the earlier rows often; the deferred order reads each row twice in
-all.  All arithmetic runs in the library's kernels.
+every call, and ``current()`` decodes them in place (the code buffers are
+laid out for the whole segment; the decode reads the first rows).  Ranges
+keep widening while the segment is short, so this re-reads the earlier rows
+often; the deferred order reads each row twice in all.  All arithmetic runs
+in the library's kernels.
 """
 from __future__ import annotations
 
@@ -75,6 +77,19 @@ class ChunkedVisualQuantizer:
                     cq_quantize_kv_rows(self._cache(L), 0, t, self.bits, L, mn, mx, self.n, codes, scale, minv,
                                         unit_mask=self.grew[L], row0=self.row0)
         self.t += m
+
+    def current(self) -> QuantizedVisualKV:
+        """The segment so far (eager codes only): its t rows in code buffers
+        laid out for all n, for a decode between appends."""
+        if not self.eager:
+            raise ValueError("the segment so far is coded only with eager=True")
+        if self.t == 0:
+            raise ValueError("no rows appended yet")
+        if self.t != self.n and self.n % 32:
+            raise ValueError(f"code buffers laid out for {self.n} tokens: a decode before the end needs a multiple "
+                             "of 32")
+        return QuantizedVisualKV.from_codes(self.out[CQ_LAYOUT_K], self.out[CQ_LAYOUT_V], self.t, self.bits,
+                                            n_cap=self.n)
 
     def finish(self) -> QuantizedVisualKV:
         """The quantized segment (all n rows must have been appended)."""

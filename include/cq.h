@@ -57,7 +57,7 @@
 extern "C" {
 #endif
 
-#define CQ_ABI_VERSION 2
+#define CQ_ABI_VERSION 3
 
 typedef enum {
   CQ_OK = 0,
@@ -88,11 +88,12 @@ typedef struct {
 } cq_calib;
 
 /* Execution path selection, for tests and tuning (NULL opts = automatic).
- * CQ_PATH_FAST picks one of the matrix-core decode schedules itself: at b = 1
- * the LDS-score one when it takes the shape and every (batch, kv head) unit
- * gets a workgroup (a CU) of its own (at most 256 units on a 256-CU MI355X),
- * else the split one below 64 units, else the one-launch one.  The FAST_
- * values force one (decode only; for quantization they mean CQ_PATH_FAST):
+ * CQ_PATH_FAST picks one of the matrix-core decode schedules itself: at b = 1,
+ * when every (batch, kv head) unit gets a workgroup (a CU) of its own (at most
+ * 256 units on a 256-CU MI355X), the all-in-flight one if it takes the shape,
+ * else the LDS-score one; otherwise the split one below 64 units, else the
+ * one-launch one.  The FAST_ values force one (decode only; for quantization
+ * they mean CQ_PATH_FAST):
  *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head);
  *   CQ_PATH_FAST_SPLIT  b = 1 only: a key-pass launch and a value-pass launch,
  *                       each over token chunks of every (batch, kv head);
@@ -111,12 +112,19 @@ typedef struct {
  *                       and tail are formed in another order, so its results
  *                       match CQ_PATH_FAST_ONE's to the 2e-3 tolerance, not
  *                       bit for bit.  Needs no workspace.
+ *   CQ_PATH_FAST_WIDE   b = 1 only, G in {1, 2, 4}, n <= 4096 a multiple of
+ *                       32, T <= 256: one launch, one workgroup per (batch,
+ *                       kv head) that requests all of its code tiles at once
+ *                       and keeps the scores in registers (the keys are read
+ *                       once); meant for at most one unit per CU.  Results
+ *                       equal CQ_PATH_FAST_ONE's bit for bit.  Needs no
+ *                       workspace.
  * At b = 1 the one-launch, LDS-score and pipelined paths take the query as
  * four balanced base-31 digits (about 20 bits); the split path and b > 1 as a
  * 22-bit fixed-point integer. */
 typedef enum {
   CQ_PATH_AUTO = 0, CQ_PATH_GENERIC = 1, CQ_PATH_FAST = 2, CQ_PATH_FAST_ONE = 3, CQ_PATH_FAST_SPLIT = 4,
-  CQ_PATH_FAST_LDS = 5, CQ_PATH_FAST_PIPE = 6
+  CQ_PATH_FAST_LDS = 5, CQ_PATH_FAST_PIPE = 6, CQ_PATH_FAST_WIDE = 7
 } cq_path;
 typedef struct {
   int32_t path;     /* cq_path; a FAST path on an unsupported shape -> CQ_ERR_UNSUPPORTED */
@@ -130,10 +138,20 @@ typedef struct {
                        status word reads 1); 0 = the default bound of a few seconds,
                        negative -> CQ_ERR_INVALID_ARG.  A small value forces the
                        time-out path from the host (tests). */
+  int32_t n_cap;    /* decode: the token capacity the visual code buffers are
+                       laid out for (0 = n).  With n_cap > n the K and V words
+                       are those of cq_quantize_kv / cq_quantize_kv_rows for
+                       n_cap tokens ([B][Hkv][d*bits/32][n_cap] and
+                       [B][Hkv][ceil(n_cap*bits/32)][d]) of which the first n
+                       are attended over, so a cache that grows frame by frame
+                       is decoded in place between appends.  Requires
+                       n <= n_cap and n_cap % 32 == 0 when n_cap != n, else
+                       CQ_ERR_INVALID_ARG; ignored by quantization. */
 } cq_opts;
 
 /* ABI version of the loaded library (CQ_ABI_VERSION).  Version 2 added
- * cq_opts.max_polls, CQ_ERR_TIMEOUT and cq_quantize_status. */
+ * cq_opts.max_polls, CQ_ERR_TIMEOUT and cq_quantize_status; version 3
+ * cq_opts.n_cap. */
 int32_t cq_abi_version(void);
 
 /* hipError_t of the most recent CQ_ERR_HIP returned on the calling thread

@@ -29,7 +29,7 @@ def test_header_and_exports_agree():
 
 
 def test_version_and_status_strings():
-    assert lib.cq_abi_version() == 2
+    assert lib.cq_abi_version() == 3
     for s in range(6):
         assert lib.cq_status_str(s)
     assert b"TIMEOUT" in lib.cq_status_str(5)
@@ -86,7 +86,7 @@ def _decode(**kw):
     (dict(wsb=8, opts=ctypes.pointer(cqb.cq_opts(1, 0))), 3),
     (dict(opts=ctypes.pointer(cqb.cq_opts(0, -2))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(2, 0)), Hq=64), 2),      # matrix-core path: group sizes 1, 2, 4
-    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0))), 1),              # no such path
+    (dict(opts=ctypes.pointer(cqb.cq_opts(8, 0))), 1),              # no such path
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), bits=2), 2),     # LDS-score schedule: b = 1 only ...
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), n=8320), 2),     # ... and G x ceil(n/128) <= 256
     (dict(opts=ctypes.pointer(cqb.cq_opts(5, 0)), Hq=24), 2),      # ... and G in 1, 2, 4
@@ -96,12 +96,21 @@ def _decode(**kw):
     (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), T=129), 2),      # ... T <= 128 ...
     (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), n=80), 2),       # ... n a multiple of 32
     (dict(opts=ctypes.pointer(cqb.cq_opts(6, 0)), Hq=48), 2),      # ... G in 1, 2, 4
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0)), bits=2), 2),     # all-in-flight schedule: b = 1 only ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0)), n=4128), 2),     # ... n <= 4096 ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0)), T=257), 2),      # ... T <= 256 ...
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0)), n=80), 2),       # ... n a multiple of 32
+    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0)), Hq=48), 2),      # ... G in 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),      # one-launch schedule: group sizes 1, 2, 4
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), bits=2), 2),     # split schedule: b = 1 only
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=0, kc=None, vc=None), 2),   # ... and n > 0
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=96, ws=None), 3),           # it needs a workspace
     (dict(opts=ctypes.pointer(cqb.cq_opts(4, 0)), n=96, wsb=64), 3),
     (dict(kc=ODD), 1), (dict(vc=ODD), 1), (dict(kt=ODD), 1), (dict(ws=ODD), 1), (dict(q=ctypes.c_void_p(0x10001)), 1),
+    # a code capacity below n, or one that is not a multiple of 32
+    (dict(opts=ctypes.pointer(cqb.cq_opts(0, 0, 0, 32))), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(0, 0, 0, 100))), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(0, 0, 0, -64))), 1),
 ])
 def test_decode_rejects(kw, status):
     assert _decode(**kw) == status
@@ -119,7 +128,7 @@ def _decode_noalloc(**kw):
 @pytest.mark.parametrize("kw,status", [
     (dict(q=None), 1), (dict(out=None), 1), (dict(kc=None), 1), (dict(T=0), 1), (dict(Hq=30), 1),
     (dict(bits=5), 1), (dict(d=64), 2), (dict(kc=ODD), 1),
-    (dict(opts=ctypes.pointer(cqb.cq_opts(7, 0))), 1),
+    (dict(opts=ctypes.pointer(cqb.cq_opts(8, 0))), 1),
     (dict(opts=ctypes.pointer(cqb.cq_opts(3, 0)), Hq=64), 2),
     # the generic schedule's scores of 64 x 32 heads x 8192 tokens take 64 MiB:
     # beyond the fixed scratch, refused before anything is enqueued

@@ -34,7 +34,7 @@ IDENTITY = (1.0, 0.0, 1.0, 0.0)
 
 P = cqb
 B1_PATHS = [P.CQ_PATH_GENERIC, P.CQ_PATH_AUTO, P.CQ_PATH_FAST_ONE, P.CQ_PATH_FAST_LDS, P.CQ_PATH_FAST_PIPE,
-            P.CQ_PATH_FAST_SPLIT]
+            P.CQ_PATH_FAST_SPLIT, P.CQ_PATH_FAST_WIDE]
 BN_PATHS = [P.CQ_PATH_GENERIC, P.CQ_PATH_AUTO, P.CQ_PATH_FAST_ONE]
 
 
@@ -136,6 +136,8 @@ def _takes(path, bits, G, n, T):
         return fast and bits == 1 and G * -(-n // 128) <= 256 and T <= 256
     if path == P.CQ_PATH_FAST_PIPE:
         return fast and bits == 1 and 32 <= n <= 8192 and T <= 128
+    if path == P.CQ_PATH_FAST_WIDE:
+        return fast and bits == 1 and n <= 4096 and T <= 256
     return True
 
 

@@ -57,3 +57,19 @@ def test_binding_refuses_host_tensors():
     k, _ = _caches(256)
     with pytest.raises(ValueError):
         cqb.cq_kv_range_update(k, 0, 64, reset=True)
+
+
+def test_segment_so_far_needs_eager_codes_and_rows():
+    k, v = _caches()
+    with pytest.raises(ValueError):
+        ChunkedVisualQuantizer(k, v, 512).current()            # deferred codes: nothing to decode between appends
+    with pytest.raises(ValueError):
+        ChunkedVisualQuantizer(k, v, 512, eager=True).current()    # nothing appended yet
+    q = ChunkedVisualQuantizer(k, v, 1000, eager=True)
+    q.t = 512                                                  # (as after appends of 512 rows)
+    with pytest.raises(ValueError):
+        q.current()                                            # capacity 1000 is no multiple of 32
+    q = ChunkedVisualQuantizer(k, v, 992, eager=True)
+    q.t = 512
+    cur = q.current()
+    assert (cur.n, cur.n_cap) == (512, 992)
