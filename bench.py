@@ -34,7 +34,10 @@ Sweeps (not the headline line; one JSON line per point, then a table):
                            lengths 64 .. 4096;
                            shapes: quantize and decode of the one-layer
                            workloads (B=16 n=3328 and B=64 n=8192) on their
-                           own.  No name: all six
+                           own;
+                           small: the b = 1 decode at B = 1 .. 32 (at most
+                           one unit per CU), n = 3328 and 8192, on every
+                           schedule that takes the shape.  No name: all seven
 
 Profiling helpers (used to produce profiles/):
     --only {step,decode,copy}
@@ -437,7 +440,7 @@ def sweeps(args):
         rows.append(row)
         print(json.dumps(row), flush=True)
 
-    which = set(args.sweeps) or {"bits", "budget", "graph", "stream", "tail", "shapes"}
+    which = set(args.sweeps) or {"bits", "budget", "graph", "stream", "tail", "shapes", "small"}
     layers, Hq, Hkv, d, T = 32, 32, 8, 128, 64
     calib = (0.9, 0.0, 0.8, 0.0)
 
@@ -476,6 +479,49 @@ def sweeps(args):
               "GBs": round(nb / t / 1e9, 1), "frac_8TBs": round(nb / t / 1e9 / HBM_PEAK_GBS, 4)})
         del K, V, kt, vt, q, out, Kf, Vf, fws, scratch
         torch.cuda.empty_cache()
+
+    def small_sweep():
+        """b = 1 decode at one unit per CU or fewer (B = 1 .. 32, 32q/8kv, T = 64,
+        n = 3328 and 8192), every schedule that takes the shape, with the
+        Infinity Cache flushed before each call"""
+        scratch = Flush(dev)
+        paths = {"auto": cqb.CQ_PATH_AUTO, "one": cqb.CQ_PATH_FAST_ONE, "lds": cqb.CQ_PATH_FAST_LDS,
+                 "wide": cqb.CQ_PATH_FAST_WIDE, "pipe": cqb.CQ_PATH_FAST_PIPE, "split": cqb.CQ_PATH_FAST_SPLIT}
+        for n in (3328, 8192):
+            Bmax = 32
+            K = kv_torch(7, 0, ROLE_K, Bmax, Hkv, n, d, "float16", dev)
+            V = kv_torch(7, 0, ROLE_V, Bmax, Hkv, n, d, "float16", dev)
+            kc_all, ks_all, km_all = cqb.cq_quantize_kv(K, 1, cqb.CQ_LAYOUT_K)
+            vc_all, vs_all, vm_all = cqb.cq_quantize_kv(V, 1, cqb.CQ_LAYOUT_V)
+            del K, V
+            kt_all = kv_torch(7, 0, ROLE_KTAIL, Bmax, Hkv, T, d, "float16", dev)
+            vt_all = kv_torch(7, 0, ROLE_VTAIL, Bmax, Hkv, T, d, "float16", dev)
+            q_all = q_torch(7, 0, Bmax, Hq, d, "float16", dev)
+            for B in (1, 2, 4, 8, 16, 32):
+                cfg = Config(f"small_B{B}_n{n}", B=B, Hq=Hq, Hkv=Hkv, n=n, T=T, seed=7)
+                kc, ks, km, vc, vs, vm, kt, vt, q = (x[:B] for x in (kc_all, ks_all, km_all, vc_all, vs_all, vm_all,
+                                                                      kt_all, vt_all, q_all))
+                out = torch.empty((B, Hq, d), dtype=torch.float16, device=dev)
+                ws = torch.empty(max(1, cqb.lib.cq_decode_attn_workspace(B, Hq, Hkv, n, T, d, 1)),
+                                 dtype=torch.uint8, device=dev)
+                row = {"sweep": "small", "B": B, "n": n, "T": T}
+                for name, path in paths.items():
+                    note(f"small B={B} n={n} {name}")
+                    try:
+                        t = timed(lambda: cqb.cq_decode_attn(q, kc, ks, km, vc, vs, vm, kt, vt, n=n, bits=1,
+                                                             sm_scale=sm, calib=calib, out=out, workspace=ws,
+                                                             path=path), args.steps, scratch)
+                    except cqb.CQError:
+                        continue                       # the schedule does not take the shape
+                    row[name + "_us"] = round(t * 1e6, 2)
+                nb = decode_bytes(cfg)
+                best = min(v for k, v in row.items() if k.endswith("_us"))
+                row["auto_frac_8TBs"] = round(nb / (row["auto_us"] * 1e-6) / 1e9 / HBM_PEAK_GBS, 4)
+                row["best_us"] = best
+                emit(row)
+            del kc_all, ks_all, km_all, vc_all, vs_all, vm_all, kt_all, vt_all, q_all
+            torch.cuda.empty_cache()
+        del scratch
 
     def tail_sweep():
         """B=64, n=8192, one layer, decode with the Infinity Cache flushed at
@@ -677,6 +723,8 @@ def sweeps(args):
         tail_sweep()
     if "shapes" in which:
         shapes_sweep()
+    if "small" in which:
+        small_sweep()
     if "stream" in which:
         stream_sweep()
 
@@ -692,6 +740,11 @@ def sweeps(args):
             pt, ms = f"{r['mode']}, chunk {r['chunk']}, n={r['n']}", r["ms"]
         elif r["sweep"] == "tail":
             pt, ms = f"T={r['T']}, n={r['n']}", r["decode_ms"]
+        elif r["sweep"] == "small":
+            paths = ", ".join(f"{k[:-3]} {v}" for k, v in r.items() if k.endswith("_us") and k != "best_us")
+            print(f"| small | n={r['n']}: {paths} (us) | {r['B']} | {r['auto_us'] / 1e3:.4f} | "
+                  f"{round(r['B'] / (r['auto_us'] * 1e-6), 1)} | - | {r['auto_frac_8TBs']} |", file=sys.stderr)
+            continue
         elif r["sweep"] == "shapes":
             print(f"| shapes | {r['workload']} quantize | {r['B']} | {r['quantize_ms']} | - | {r['quantize_GBs']} | "
                   f"{r['quantize_frac_8TBs']} |", file=sys.stderr)
@@ -794,7 +847,7 @@ def main():
                                                        "fast_wide", "generic"],
                     help="decode schedule for --only decode")
     ap.add_argument("--summarize", nargs="+", default=None, metavar="DIR")
-    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream", "tail", "shapes"],
+    ap.add_argument("--sweeps", nargs="*", choices=["bits", "budget", "graph", "stream", "tail", "shapes", "small"],
                     default=None)
     ap.add_argument("--command-note", default="")
     ap.add_argument("--profile-name", default=None, help="profiles/<name>_<workload>.md for --summarize")

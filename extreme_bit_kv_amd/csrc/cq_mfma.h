@@ -108,4 +108,77 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
+// ---- reductions across lanes in the VALU ------------------------------
+// __shfl_xor compiles to ds_bpermute here: one round trip through the LDS unit
+// per step, and a chain of them costs about a hundred cycles a step on a busy
+// CU.  DPP row rotations and lane reads stay in the VALU.
+
+// x rotated by R lanes within each row of 16 lanes (DPP row_ror)
+template <int R>
+__device__ __forceinline__ float ror16(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x120 + R, 0xF, 0xF,
+                                                               false));
+}
+template <int R>
+__device__ __forceinline__ double ror16(double x) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const int lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, 0x120 + R, 0xF, 0xF, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), 0x120 + R, 0xF, 0xF, false);
+  return __builtin_bit_cast(double, ((unsigned long long)(uint32_t)hi << 32) | (uint32_t)lo);
+}
+
+// Over each row of 16 lanes, in every lane of the row.  Rotations by 8, 4, 2
+// and 1 lanes: lane i adds the value of lane i + R (mod 16), which after the
+// earlier steps equals that of lane i ^ R, so a sum is formed by the same
+// additions, operand for operand, as an xor butterfly over 8, 4, 2, 1.
+template <typename F>
+__device__ __forceinline__ F row_sum16(F x) {
+  x += ror16<8>(x);
+  x += ror16<4>(x);
+  x += ror16<2>(x);
+  x += ror16<1>(x);
+  return x;
+}
+__device__ __forceinline__ float row_min16(float x) {
+  x = fminf(x, ror16<8>(x));
+  x = fminf(x, ror16<4>(x));
+  x = fminf(x, ror16<2>(x));
+  return fminf(x, ror16<1>(x));
+}
+__device__ __forceinline__ float row_max16(float x) {
+  x = fmaxf(x, ror16<8>(x));
+  x = fmaxf(x, ror16<4>(x));
+  x = fmaxf(x, ror16<2>(x));
+  return fmaxf(x, ror16<1>(x));
+}
+
+__device__ __forceinline__ float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ __forceinline__ double lane_d(double x, int l) {
+  const unsigned long long u = __builtin_bit_cast(unsigned long long, x);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)u, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(u >> 32), l);
+  return __builtin_bit_cast(double, ((unsigned long long)hi << 32) | lo);
+}
+
+// Over the 64 lanes of the wave (every lane receives it; all lanes active):
+// each row of 16, then the four rows as ((r0 + r1) + (r2 + r3)).
+__device__ __forceinline__ float wave_sum(float x) {
+  x = row_sum16(x);
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
+}
+__device__ __forceinline__ double wave_sum(double x) {
+  x = row_sum16(x);
+  return (lane_d(x, 0) + lane_d(x, 16)) + (lane_d(x, 32) + lane_d(x, 48));
+}
+__device__ __forceinline__ float wave_min(float x) {
+  x = row_min16(x);
+  return fminf(fminf(lane_f(x, 0), lane_f(x, 16)), fminf(lane_f(x, 32), lane_f(x, 48)));
+}
+__device__ __forceinline__ float wave_max(float x) {
+  x = row_max16(x);
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
+}
+
 }  // namespace cqm

@@ -197,10 +197,7 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
         float sc = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) sc = fmaf(s_q[hh][8 * cl + c], kf[c], sc);
-        sc += __shfl_xor(sc, 8);
-        sc += __shfl_xor(sc, 4);
-        sc += __shfl_xor(sc, 2);
-        sc += __shfl_xor(sc, 1);
+        sc = cqm::row_sum16(sc);
         if (cl == 0) s_ts[hh][j - c0] = j < T ? sc : -INFINITY;
       }
     }
@@ -209,8 +206,7 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
       const int hh = wave;
       float cm = -INFINITY;
       for (int t = lane; t < kMaxTail; t += 64) cm = fmaxf(cm, s_ts[hh][t]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cm = fmaxf(cm, __shfl_xor(cm, off));
+      cm = cqm::wave_max(cm);
       if (lane == 0) s_cm[hh] = cm;
     }
     cqm::lds_barrier();
@@ -228,8 +224,7 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
         s_ts[hh][t] = pw;
         cs += pw;
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) cs += __shfl_xor(cs, off);
+      cs = cqm::wave_sum(cs);
       if (lane == 0) s_cs[hh] = cs;
     }
     cqm::lds_barrier();
@@ -300,7 +295,6 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   __builtin_amdgcn_s_setprio(3);
 
   __shared__ float s_q[4][128];                 // sm * q, float
-  __shared__ float s_qp[4][128];                // sm * q * scale_K
   __shared__ double s_c0[4];
   __shared__ int s_F[4];
   __shared__ __align__(16) uint32_t s_adig[4][4][32];   // K-side fp6 digit codes: [head][plane][128 k slots]
@@ -325,17 +319,23 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
   const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
   // The prologue's inputs are requested before any prefetch: vector loads
-  // complete in order, so the prologue then waits for these alone.  Thread:
-  // head ph (heads past G read head G - 1, unused), channel pj; the scales and
-  // minima of an empty cache are read at the zero block.
-  const int ph = tid >> 7, pj = tid & 127;
+  // complete in order, so the prologue then waits for these alone.  Wave w < 4
+  // takes head w (heads past G read head G - 1, unused) at channels lane and
+  // lane + 64, so that each head's statistics and digits stay within one wave;
+  // waves 4 and 5 stage scale_V and min_V.  Every lane loads all of it (no
+  // load under a branch); an empty cache's scales and minima are read at the
+  // zero block.
   const float* ksb = n > 0 ? P.ks : reinterpret_cast<const float*>(g_pad);
   const float* kmb = n > 0 ? P.km : reinterpret_cast<const float*>(g_pad);
   const float* vsb = n > 0 ? P.vs : reinterpret_cast<const float*>(g_pad);
   const float* vmb = n > 0 ? P.vm : reinterpret_cast<const float*>(g_pad);
-  const size_t prm = n > 0 ? (size_t)unit * 128 + pj : (size_t)pj;
-  const float q_in = ld_any(P.q, ((size_t)b * P.Hq + h * G + min(ph, G - 1)) * 128 + pj, F32);
-  const float ks_in = ksb[prm], km_in = kmb[prm], vs_in = vsb[prm], vm_in = vmb[prm];
+  const size_t prm = n > 0 ? (size_t)unit * 128 : 0;
+  const size_t qrow = ((size_t)b * P.Hq + h * G + min(wave & 3, G - 1)) * 128;
+  const float q_lo = ld_any(P.q, qrow + lane, F32), q_hi = ld_any(P.q, qrow + lane + 64, F32);
+  const float ks_lo = ksb[prm + lane], ks_hi = ksb[prm + lane + 64];
+  const float km_lo = kmb[prm + lane], km_hi = kmb[prm + lane + 64];
+  const int vj = lane + 64 * (wave & 1);
+  const float vs_in = vsb[prm + vj], vm_in = vmb[prm + vj];
   // Code tiles are read with buffer loads: one descriptor per unit and tensor,
   // a fixed byte offset per lane plus the tile's (wave-uniform); a tile past
   // the last reads out of range, which returns zeros without any traffic.
@@ -421,80 +421,69 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     s_next[0] = 2 * kWaves;
     s_next[1] = kWaves;
   }
-  if (tid < 4) {
-    s_psum[tid] = 0.0;
-    s_kc[tid] = 0.f;
-  }
+  if (tid < 4) s_psum[tid] = 0.0;
   for (int i = tid; i < 4 * 128; i += kThreads) (&s_vsum[0][0])[i] = 0ull;
 
   // ---- prologue: post-scaled query, fixed-point digits -------------------
-  __shared__ double s_c0p[8];
-  __shared__ float s_mqp[8];
-  {                                             // thread: head ph, channel pj
-    const int hh = ph, j = pj;
-    float qv = 0.f, qp = 0.f;
-    double pr = 0.0;
+  // Wave hh < 4 settles head hh alone (one barrier in all): sm q and
+  // q' = sm q * scale_K, the offset c0 = sm q . min_K (the sums of channels
+  // 0..63 and 64..127, each over the wave, then added), F from max |q'|, and
+  // Q = round(q' 2^F) in four balanced base-31 digits.  Channel j sits in k
+  // slot 32 (j / 32) + 8 R + 2 (e mod 4) + e / 16 of its row, e = j mod 32,
+  // R = (e / 4) mod 4, the fp4 field of its key bit; its digit is stored as
+  // d / 2, d / 4, d / 8 or -d / 8 (the bit-3 fields read +-1: 1 - 2 c), so
+  // that every product is d c / 4 and the bit-3 channels leave a constant
+  // sum of -Q / 8, added back to the head's offset.
+  if (wave < 4) {
+    const int hh = wave;
+    float qv[2] = {0.f, 0.f}, qp[2] = {0.f, 0.f};
+    double pr[2] = {0.0, 0.0};
     if (hh < G) {
-      qv = P.sm * q_in;
-      qp = qv * ks_in;
-      pr = (double)qv * (double)km_in;
+      qv[0] = P.sm * q_lo;
+      qv[1] = P.sm * q_hi;
+      qp[0] = qv[0] * ks_lo;
+      qp[1] = qv[1] * ks_hi;
+      pr[0] = (double)qv[0] * (double)km_lo;
+      pr[1] = (double)qv[1] * (double)km_hi;
     }
-    s_q[hh][j] = qv;
-    s_qp[hh][j] = qp;
-    if (hh == 0) {
-      s_vs[j] = vs_in;
-      s_vm[j] = vm_in;
-    }
-    float aq = fabsf(qp);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      pr += __shfl_xor(pr, off);
-      aq = fmaxf(aq, __shfl_xor(aq, off));
-    }
-    if (lane == 0) {
-      s_c0p[wave] = pr;
-      s_mqp[wave] = aq;
-    }
-  }
-  lds_barrier();
-  if (tid < 4) {
-    const double c0 = s_c0p[2 * tid] + s_c0p[2 * tid + 1];
-    const float mq = fmaxf(s_mqp[2 * tid], s_mqp[2 * tid + 1]);
+    s_q[hh][lane] = qv[0];
+    s_q[hh][lane + 64] = qv[1];
+    const double c0 = cqm::wave_sum(pr[0]) + cqm::wave_sum(pr[1]);
+    const float mq = cqm::wave_max(fmaxf(fabsf(qp[0]), fabsf(qp[1])));
     int F = 0;
     if (mq > 0.f) {
       const int e = ilogbf(mq);
       F = ldexpf(mq, 18 - e) > (float)kQMax ? 17 - e : 18 - e;
     }
-    s_F[tid] = F;
-    s_c0[tid] = c0;
-  }
-  lds_barrier();
-  {
-    // Q = round(q' 2^F) in four balanced base-31 digits.  Channel j sits in k
-    // slot 32 (j / 32) + 8 R + 2 (e mod 4) + e / 16 of its row, e = j mod 32,
-    // R = (e / 4) mod 4, the fp4 field of its key bit; its digit is stored as
-    // d / 2, d / 4, d / 8 or -d / 8 (the bit-3 fields read +-1: 1 - 2 c), so
-    // that every product is d c / 4 and the bit-3 channels leave a constant
-    // sum of -Q / 8, added back to the head's offset.
-    const int hh = tid >> 7, j = tid & 127;
-    const float x = rintf(ldexpf(s_qp[hh][j], s_F[hh]));            // |x| <= kQMax, exact
-    float d[4], r = x;
-#pragma unroll
-    for (int k = 3; k > 0; --k) {
-      const float qk = rintf(r * (1.f / 31.f));                      // exact: r / 31 is never near a half
-      d[k] = fmaf(-31.f, qk, r);
-      r = qk;
-    }
-    d[0] = r;
-    const int e = j & 31, Rf = (e >> 2) & 3, slot = 32 * (j >> 5) + 8 * Rf + 2 * (e & 3) + (e >> 4);
-    const int mult = Rf == 0 ? 4 : (Rf == 1 ? 2 : (Rf == 2 ? 1 : -1));
     unsigned char* ad = reinterpret_cast<unsigned char*>(&s_adig[hh][0][0]);
+    float kcs = 0.f;
 #pragma unroll
-    for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + slot] = (unsigned char)enc6((int)d[pl] * mult);
-    float kcs = Rf == 3 ? 0.125f * x : 0.f;                          // multiples of 1/8 below 2^21: exact
+    for (int c = 0; c < 2; ++c) {
+      const int j = lane + 64 * c;
+      const float x = rintf(ldexpf(qp[c], F));                       // |x| <= kQMax, exact
+      float d[4], r = x;
 #pragma unroll
-    for (int off = 32; off > 0; off >>= 1) kcs += __shfl_xor(kcs, off);
-    if (lane == 0 && hh < G) atomicAdd(&s_kc[hh], kcs);
+      for (int k = 3; k > 0; --k) {
+        const float qk = rintf(r * (1.f / 31.f));                    // exact: r / 31 is never near a half
+        d[k] = fmaf(-31.f, qk, r);
+        r = qk;
+      }
+      d[0] = r;
+      const int e = j & 31, Rf = (e >> 2) & 3, slot = 32 * (j >> 5) + 8 * Rf + 2 * (e & 3) + (e >> 4);
+      const int mult = Rf == 0 ? 4 : (Rf == 1 ? 2 : (Rf == 2 ? 1 : -1));
+#pragma unroll
+      for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + slot] = (unsigned char)enc6((int)d[pl] * mult);
+      kcs += Rf == 3 ? 0.125f * x : 0.f;                             // multiples of 1/8 below 2^21: exact
+    }
+    kcs = cqm::wave_sum(kcs);
+    if (lane == 0) {
+      s_F[hh] = F;
+      s_c0[hh] = c0;
+      s_kc[hh] = hh < G ? kcs : 0.f;
+    }
+  } else if (wave < 6) {
+    s_vs[vj] = vs_in;
+    s_vm[vj] = vm_in;
   }
   lds_barrier();
 
@@ -510,10 +499,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
+        s = cqm::row_sum16(s);
         if (cl == 0 && j < Tf) s_ts[hh][j] = s;
       }
     };
@@ -634,11 +620,8 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     load_vtail();
   }
   // ---- min / max of every head's visual scores ---------------------------
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    vmin = fminf(vmin, __shfl_xor(vmin, off));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-  }
+  vmin = cqm::row_min16(vmin);
+  vmax = cqm::row_max16(vmax);
   if ((lane & 15) == 0) {
     s_red[wave][oh][0] = vmin;
     s_red[wave][oh][1] = vmax;
@@ -650,12 +633,9 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
     float tmax = -INFINITY;
     for (int j = lane; j < Tf; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      m = fminf(m, __shfl_xor(m, off));
-      M = fmaxf(M, __shfl_xor(M, off));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, off));
-    }
+    m = cqm::wave_min(m);
+    M = cqm::wave_max(M);
+    tmax = cqm::wave_max(tmax);
     // scores are in units of scale = 4 2^-F, offset by q . min_K plus the
     // bit-3 constant; the exponent of a visual weight is lam s + mu
     const double scale = ldexp(4.0, -s_F[hh]);
@@ -687,8 +667,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
       s_ts[hh][j] = pj;
       pt += pj;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
+    pt = cqm::wave_sum(pt);
     if (lane == 0) s_ptail[hh] = pt;
   }
   lds_barrier();
@@ -830,8 +809,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   // the exact integer 2^7 sum_i P_i c_i, and the waves add theirs with 64-bit
   // LDS atomics: exact, so the order in which waves arrive does not matter.
   flush();
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
+  psum = cqm::row_sum16(psum);
   if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
   lds_barrier();
   if constexpr (LT) {
@@ -1019,11 +997,8 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
         s_vm[j] = vm_in;
       }
       float aq = fabsf(qp);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        pr += __shfl_xor(pr, off);
-        aq = fmaxf(aq, __shfl_xor(aq, off));
-      }
+      pr = cqm::wave_sum(pr);
+      aq = cqm::wave_max(aq);
       if (lane == 0) {
         s_c0p[wave] = pr;
         s_mqp[wave] = aq;
@@ -1059,8 +1034,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 #pragma unroll
       for (int pl = 0; pl < 4; ++pl) ad[pl * 128 + slot] = (unsigned char)enc6((int)d[pl] * mult);
       float kcs = Rf == 3 ? 0.125f * x : 0.f;
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) kcs += __shfl_xor(kcs, off);
+      kcs = cqm::wave_sum(kcs);
       if (lane == 0 && hh < G) atomicAdd(&s_kc[hh], kcs);
     }
     lds_barrier();
@@ -1074,10 +1048,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
           float s = 0.f;
 #pragma unroll
           for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-          s += __shfl_xor(s, 8);
-          s += __shfl_xor(s, 4);
-          s += __shfl_xor(s, 2);
-          s += __shfl_xor(s, 1);
+          s = cqm::row_sum16(s);
           if (cl == 0 && j < T) s_ts[hh][j] = s;
         }
       };
@@ -1195,11 +1166,8 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       }
     }
     // ---- statistics ---------------------------------------------------------
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      vmin = fminf(vmin, __shfl_xor(vmin, off));
-      vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-    }
+    vmin = cqm::row_min16(vmin);
+    vmax = cqm::row_max16(vmax);
     if ((lane & 15) == 0) {
       s_red[wave][oh][0] = vmin;
       s_red[wave][oh][1] = vmax;
@@ -1211,12 +1179,9 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       float M = lane < kWavesL ? s_red[lane][hh][1] : -INFINITY;
       float tmax = -INFINITY;
       for (int j = lane; j < T; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) {
-        m = fminf(m, __shfl_xor(m, off));
-        M = fmaxf(M, __shfl_xor(M, off));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, off));
-      }
+      m = cqm::wave_min(m);
+      M = cqm::wave_max(M);
+      tmax = cqm::wave_max(tmax);
       const double scale = ldexp(4.0, -s_F[hh]);   // the statistics of df_b1, computed the same way
       const double c0 = s_c0[hh] + (double)s_kc[hh] * scale;
       double lam = scale, mu = -scale * (double)M, vis_max = (double)M * scale + c0;
@@ -1243,8 +1208,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
         s_ts[hh][j] = pj2;
         ptl += pj2;
       }
-#pragma unroll
-      for (int off = 32; off > 0; off >>= 1) ptl += __shfl_xor(ptl, off);
+      ptl = cqm::wave_sum(ptl);
       if (lane == 0) s_ptail[hh] = ptl;
     }
     lds_barrier();
@@ -1386,8 +1350,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
     // ---- combine planes, reduce over waves --------------------------------------
     __builtin_amdgcn_s_setprio(1);
     flush();
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
+    psum = cqm::row_sum16(psum);
     if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
     lds_barrier();
     if (tid < G * 128) {
@@ -1498,11 +1461,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     s_q[hh][j] = qv;
     s_qp[hh][j] = qp;
     float aq = fabsf(qp);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      pr += __shfl_xor(pr, off);
-      aq = fmaxf(aq, __shfl_xor(aq, off));
-    }
+    pr = cqm::wave_sum(pr);
+    aq = cqm::wave_max(aq);
     if (lane == 0) {
       s_c0p[wave] = pr;
       s_mqp[wave] = aq;
@@ -1652,10 +1612,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
         float s = 0.f;
 #pragma unroll
         for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-        s += __shfl_xor(s, 8);
-        s += __shfl_xor(s, 4);
-        s += __shfl_xor(s, 2);
-        s += __shfl_xor(s, 1);
+        s = cqm::row_sum16(s);
         if (cl == 0 && j < Tf) s_ts[hh][j] = s;
       }
     };
@@ -1687,11 +1644,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) {
-    vmin = fminf(vmin, __shfl_xor(vmin, off));
-    vmax = fmaxf(vmax, __shfl_xor(vmax, off));
-  }
+  vmin = cqm::row_min16(vmin);
+  vmax = cqm::row_max16(vmax);
   if ((lane & 15) == 0) {
     s_red[wave][oh][0] = vmin;
     s_red[wave][oh][1] = vmax;
@@ -1703,12 +1657,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     float M = lane < kWaves ? s_red[lane][hh][1] : -INFINITY;
     float tmax = -INFINITY;
     for (int j = lane; j < Tf; j += 64) tmax = fmaxf(tmax, s_ts[hh][j]);
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) {
-      m = fminf(m, __shfl_xor(m, off));
-      M = fmaxf(M, __shfl_xor(M, off));
-      tmax = fmaxf(tmax, __shfl_xor(tmax, off));
-    }
+    m = cqm::wave_min(m);
+    M = cqm::wave_max(M);
+    tmax = cqm::wave_max(tmax);
     float lam = 1.f, mu = 0.f, vis_max = M;
     if (P.calib_on && n > 0) {
       const float t_lo = P.a_lo * m + P.c_lo, t_hi = P.a_hi * M + P.c_hi;
@@ -1735,8 +1686,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       s_ts[hh][j] = pj;
       pt += pj;
     }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1) pt += __shfl_xor(pt, off);
+    pt = cqm::wave_sum(pt);
     if (lane == 0) s_ptail[hh] = pt;
   }
   lds_barrier();
@@ -1862,8 +1812,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
                          16777216ll * vacc[ct][3];
     s_vred[wave][oh][8 * i16 + ct] = (float)((double)sv * (1.0 / 134217728.0));   // 2^-27
   }
-#pragma unroll
-  for (int off = 1; off < 16; off <<= 1) psum += __shfl_xor(psum, off);
+  psum = cqm::row_sum16(psum);
   if ((lane & 15) == 0) s_psum[wave][oh] = psum;
   lds_barrier();
   if constexpr (LT) {
