@@ -139,6 +139,20 @@ __device__ __forceinline__ F row_sum16(F x) {
   x += ror16<1>(x);
   return x;
 }
+// N row sums at once, the steps of the N sums interleaved so that each DPP
+// read is not right behind the write it depends on (same additions as N
+// separate row_sum16 calls)
+template <int N>
+__device__ __forceinline__ void row_sum16x(float (&x)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += ror16<8>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += ror16<4>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += ror16<2>(x[i]);
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] += ror16<1>(x[i]);
+}
 __device__ __forceinline__ float row_min16(float x) {
   x = fminf(x, ror16<8>(x));
   x = fminf(x, ror16<4>(x));

@@ -398,17 +398,16 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   };
   // the key pass keeps two tiles of look-ahead per wave (kn, km), the value
   // pass one (kn, vn); the first two are requested under the prologue.  With
-  // TPW > 0 every tile of the wave is requested here: keys, the tail values,
-  // then values (the order in which they are used).
+  // TPW > 0 every key tile of the wave is requested here, and the tail values
+  // and value tiles right after the prologue (issued together with these, they
+  // would delay the prologue's own inputs, which queue behind every CU's
+  // requests).
   uint4 kn0, kn1, km0, km1;
   constexpr int kSlots = TPW > 0 ? TPW : 1;
   uint4 kwide[kSlots][2], vwide[kSlots][2];
   if constexpr (TPW > 0) {
 #pragma unroll
     for (int k = 0; k < TPW; ++k) load_k(wave + kWaves * k, kwide[k][0], kwide[k][1]);
-    load_vtail();
-#pragma unroll
-    for (int k = 0; k < TPW; ++k) load_v(wave + kWaves * k, vwide[k][0], vwide[k][1]);
   } else {
     load_k(wave, kn0, kn1);
     load_k(wave + kWaves, km0, km1);
@@ -486,6 +485,11 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     s_vm[vj] = vm_in;
   }
   lds_barrier();
+  if constexpr (TPW > 0) {
+    load_vtail();
+#pragma unroll
+    for (int k = 0; k < TPW; ++k) load_v(wave + kWaves * k, vwide[k][0], vwide[k][1]);
+  }
 
   // ---- text tail scores ---------------------------------------------------
   // The prefetched rounds run straight (no early exit: every lane's rows were
@@ -494,13 +498,17 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   {
     const int sub = tsub, cl = tcl;
     auto tail_scores = [&](int j, const float (&kf)[8]) {
+      float sc[G];                                   // the heads' sums side by side
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float s = 0.f;
+        sc[hh] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-        s = cqm::row_sum16(s);
-        if (cl == 0 && j < Tf) s_ts[hh][j] = s;
+        for (int c = 0; c < 8; ++c) sc[hh] = fmaf(s_q[hh][8 * cl + c], kf[c], sc[hh]);
+      }
+      cqm::row_sum16x(sc);
+      if (cl == 0 && j < Tf) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s_ts[hh][j] = sc[hh];
       }
     };
 #pragma unroll
@@ -614,10 +622,10 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   // alive instead of recomputing it.)
   asm("" : "+s"(kc));
   uint4 vn0, vn1;
-  if constexpr (TPW == 0) {
+  if constexpr (TPW == 0) {                     // the tail values first: they are used first
+    load_vtail();
     load_k(wave, kn0, kn1);
     load_v(wave, vn0, vn1);
-    load_vtail();
   }
   // ---- min / max of every head's visual scores ---------------------------
   vmin = cqm::row_min16(vmin);
@@ -677,21 +685,23 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
+      // (a select, not a branch: a token past T weighs 0, and the heads'
+      // weights of every token are read together)
       const int t = vph + kPhases * i;
-      if (t < Tf) {
-        float v0, v1;
-        if constexpr (F32) {
-          v0 = __uint_as_float(vtr[i][0]);
-          v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
-        } else {
-          v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
-          v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
-        }
+      const bool tok = t < Tf;
+      float v0, v1;
+      if constexpr (F32) {
+        v0 = __uint_as_float(vtr[i][0]);
+        v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
+      } else {
+        v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
+        v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
+      }
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-          ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
-        }
+      for (int hh = 0; hh < G; ++hh) {
+        const float w = tok ? s_ts[hh][t] : 0.f;
+        ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+        ta[hh][1] = fmaf(w, v1, ta[hh][1]);
       }
     }
     for (int t = kPreTail + vph; t < Tf; t += kPhases) {
@@ -1043,13 +1053,17 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
     {
       const int sub = tsub, cl = tcl;
       auto tail_scores = [&](int j, const float (&kf)[8]) {
+        float sc[G];                                   // the heads' sums side by side
 #pragma unroll
         for (int hh = 0; hh < G; ++hh) {
-          float s = 0.f;
+          sc[hh] = 0.f;
 #pragma unroll
-          for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-          s = cqm::row_sum16(s);
-          if (cl == 0 && j < T) s_ts[hh][j] = s;
+          for (int c = 0; c < 8; ++c) sc[hh] = fmaf(s_q[hh][8 * cl + c], kf[c], sc[hh]);
+        }
+        cqm::row_sum16x(sc);
+        if (cl == 0 && j < T) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) s_ts[hh][j] = sc[hh];
         }
       };
 #pragma unroll
@@ -1216,21 +1230,23 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
       for (int i = 0; i < kPreTail / kPhases; ++i) {
+        // (a select, not a branch: a token past T weighs 0, and the heads'
+        // weights of every token are read together)
         const int t = vph + kPhases * i;
-        if (t < T) {
-          float v0, v1;
-          if constexpr (F32) {
-            v0 = __uint_as_float(vtr[i][0]);
-            v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
-          } else {
-            v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
-            v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
-          }
+        const bool tok = t < T;
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = __uint_as_float(vtr[i][0]);
+          v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
+        } else {
+          v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
+          v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
+        }
 #pragma unroll
-          for (int hh = 0; hh < G; ++hh) {
-            ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-            ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
-          }
+        for (int hh = 0; hh < G; ++hh) {
+          const float w = tok ? s_ts[hh][t] : 0.f;
+          ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+          ta[hh][1] = fmaf(w, v1, ta[hh][1]);
         }
       }
       for (int t = kPreTail + vph; t < T; t += kPhases) {
@@ -1607,13 +1623,17 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   {
     const int sub = tsub, cl = tcl;
     auto tail_scores = [&](int j, const float (&kf)[8]) {
+      float sc[G];                                   // the heads' sums side by side
 #pragma unroll
       for (int hh = 0; hh < G; ++hh) {
-        float s = 0.f;
+        sc[hh] = 0.f;
 #pragma unroll
-        for (int c = 0; c < 8; ++c) s = fmaf(s_q[hh][8 * cl + c], kf[c], s);
-        s = cqm::row_sum16(s);
-        if (cl == 0 && j < Tf) s_ts[hh][j] = s;
+        for (int c = 0; c < 8; ++c) sc[hh] = fmaf(s_q[hh][8 * cl + c], kf[c], sc[hh]);
+      }
+      cqm::row_sum16x(sc);
+      if (cl == 0 && j < Tf) {
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) s_ts[hh][j] = sc[hh];
       }
     };
 #pragma unroll
@@ -1696,21 +1716,23 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
+      // (a select, not a branch: a token past T weighs 0, and the heads'
+      // weights of every token are read together)
       const int t = vph + kPhases * i;
-      if (t < Tf) {
-        float v0, v1;
-        if constexpr (F32) {
-          v0 = __uint_as_float(vtr[i][0]);
-          v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
-        } else {
-          v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
-          v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
-        }
+      const bool tok = t < Tf;
+      float v0, v1;
+      if constexpr (F32) {
+        v0 = __uint_as_float(vtr[i][0]);
+        v1 = __uint_as_float(vtr[i][F32 ? 1 : 0]);
+      } else {
+        v0 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] & 0xFFFF)));
+        v1 = __half2float(__ushort_as_half((unsigned short)(vtr[i][0] >> 16)));
+      }
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-          ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
-        }
+      for (int hh = 0; hh < G; ++hh) {
+        const float w = tok ? s_ts[hh][t] : 0.f;
+        ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+        ta[hh][1] = fmaf(w, v1, ta[hh][1]);
       }
     }
     for (int t = kPreTail + vph; t < Tf; t += kPhases) {
