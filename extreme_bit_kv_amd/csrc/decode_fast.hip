@@ -309,6 +309,13 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
   __shared__ int s_next[2];                        // next key tile of each pass
   __shared__ float s_vs[128], s_vm[128];           // scale_V, min_V
+  // Dealt tiles: the scores of the unit's first kKeep tiles stay in LDS from
+  // the key pass to the value pass ([tile][lane][token], a lane's 8 scores),
+  // so those key tiles are read once; the others are read again and their
+  // scores recomputed (same operations, so the same values).  kKeep fills
+  // the LDS that two workgroups per CU leave.
+  constexpr int kKeep = TPW == 0 ? 17 : 0;
+  __shared__ __align__(16) float s_keep[kKeep > 0 ? kKeep : 1][64][8];
 
   // operand coordinates of the 16 x 16 x 64 products
   const int i16 = lane & 15, g4 = lane >> 4;    // A/B operand lane coordinates
@@ -609,6 +616,11 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
       vmin = min3f(min3f(vmin, st[0], st[1]), min3f(st[2], st[3], st[4]), min3f(st[5], st[6], st[7]));
       vmax = max3f(max3f(vmax, st[0], st[1]), max3f(st[2], st[3], st[4]), max3f(st[5], st[6], st[7]));
     }
+    if (tile < kKeep) {
+      float4* kp = reinterpret_cast<float4*>(&s_keep[tile][lane][0]);
+      kp[0] = make_float4(st[0], st[1], st[2], st[3]);
+      kp[1] = make_float4(st[4], st[5], st[6], st[7]);
+    }
     // fold tile by tile: left free, the compiler sinks these updates past the
     // loop and keeps every tile's scores alive
     asm volatile("" : "+v"(vmin), "+v"(vmax));
@@ -624,7 +636,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   uint4 vn0, vn1;
   if constexpr (TPW == 0) {                     // the tail values first: they are used first
     load_vtail();
-    load_k(wave, kn0, kn1);
+    load_k(wave < kKeep ? ntiles : wave, kn0, kn1);   // a kept tile: an out-of-range read, no traffic
     load_v(wave, vn0, vn1);
   }
   // ---- min / max of every head's visual scores ---------------------------
@@ -801,10 +813,17 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     if (lane == 0) nxt = atomicAdd(&s_next[1], 1);
     nxt = __builtin_amdgcn_readfirstlane(nxt);
     const uint4 kw0 = kn0, kw1 = kn1, vw0 = vn0, vw1 = vn1;
-    load_k(nxt, kn0, kn1);
+    load_k(nxt < kKeep ? ntiles : nxt, kn0, kn1);
     load_v(nxt, vn0, vn1);
     float st[8];
-    scores(kw0, kw1, st);
+    if (tile < kKeep) {
+      const float4* kp = reinterpret_cast<const float4*>(&s_keep[tile][lane][0]);
+      const float4 a = kp[0], c = kp[1];
+      st[0] = a.x; st[1] = a.y; st[2] = a.z; st[3] = a.w;
+      st[4] = c.x; st[5] = c.y; st[6] = c.z; st[7] = c.w;
+    } else {
+      scores(kw0, kw1, st);
+    }
     value_tile(tile, st, vw0, vw1);
     if (++wtiles == kFlushTiles) {
       flush();
