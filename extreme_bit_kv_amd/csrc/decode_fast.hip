@@ -57,6 +57,8 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kTile = 128;
 constexpr int kMaxTail = 256;
 constexpr int kPreTail = 64;          // tail tokens whose loads are issued early
+constexpr int kXRounds = 3;           // later tail-key rounds whose loads are in flight together
+constexpr int kXTokens = 8;           // later tail-value tokens per thread whose loads are in flight together
 constexpr float kLog2e = 1.4426950408889634f;
 
 using cqm::v4i;
@@ -536,13 +538,42 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
       }
       tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
     }
-    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves) {
-      const int j = j0 + sub;
-      float kf[8];
+    constexpr int kXR = F32 ? 1 : kXRounds;
+    // rounds past kPreTail tokens, kXR at a time: their keys are read as
+    // the prefetched ones (clamped rows, whole 16-byte pieces, no branch), the
+    // rounds' loads in flight together
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves * kXR) {
+      uint4 kr[kXR][2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
-      tail_scores(j, kf);
+      for (int x = 0; x < kXR; ++x) {
+        const size_t e = ((size_t)unit * T + max(min(j0 + 4 * kWaves * x + sub, T - 1), 0)) * 128 + 8 * cl;
+        if constexpr (F32) {
+          const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+          kr[x][0] = cqd::ld_nt(src);
+          kr[x][1] = cqd::ld_nt(src + 1);
+        } else {
+          kr[x][0] = cqd::ld_nt(reinterpret_cast<const __half*>(ktb) + e);
+          kr[x][1] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kXR; ++x) {
+        float kf[8];
+        if constexpr (F32) {
+          kf[0] = __uint_as_float(kr[x][0].x); kf[1] = __uint_as_float(kr[x][0].y);
+          kf[2] = __uint_as_float(kr[x][0].z); kf[3] = __uint_as_float(kr[x][0].w);
+          kf[4] = __uint_as_float(kr[x][1].x); kf[5] = __uint_as_float(kr[x][1].y);
+          kf[6] = __uint_as_float(kr[x][1].z); kf[7] = __uint_as_float(kr[x][1].w);
+        } else {
+          const uint32_t hw[4] = {kr[x][0].x, kr[x][0].y, kr[x][0].z, kr[x][0].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+          }
+        }
+        tail_scores(j0 + 4 * kWaves * x + sub, kf);          // rows past T: scores not stored
+      }
     }
   }
   // ---- phase 1: visual scores, their min and max -------------------------
@@ -716,13 +747,40 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
         ta[hh][1] = fmaf(w, v1, ta[hh][1]);
       }
     }
-    for (int t = kPreTail + vph; t < Tf; t += kPhases) {
-      const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
-      const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
+    constexpr int kXT = F32 ? 4 : kXTokens;
+    // tokens past kPreTail, kXT at a time: loads in flight together
+    // (clamped rows, no branch); a token past T weighs 0
+    for (int t0 = kPreTail + vph; t0 < Tf; t0 += kPhases * kXT) {
+      uint32_t vx[kXT][F32 ? 2 : 1];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-        ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+      for (int x = 0; x < kXT; ++x) {
+        const size_t e = ((size_t)unit * T + max(min(t0 + kPhases * x, T - 1), 0)) * 128 + 2 * vcp;
+        if constexpr (F32) {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+          vx[x][0] = w2.x;
+          vx[x][F32 ? 1 : 0] = w2.y;
+        } else {
+          vx[x][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kXT; ++x) {
+        const int t = t0 + kPhases * x;
+        const bool tok = t < Tf;
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = __uint_as_float(vx[x][0]);
+          v1 = __uint_as_float(vx[x][F32 ? 1 : 0]);
+        } else {
+          v0 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] & 0xFFFF)));
+          v1 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] >> 16)));
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float w = tok ? s_ts[hh][min(t, kMaxTail - 1)] : 0.f;
+          ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+          ta[hh][1] = fmaf(w, v1, ta[hh][1]);
+        }
       }
     }
 #pragma unroll
@@ -1103,13 +1161,42 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
         }
         tail_scores(4 * wave + 4 * kWavesL * r + sub, kf);
       }
-      for (int j0 = 4 * wave + 4 * kWavesL * kKtRounds; j0 < T; j0 += 4 * kWavesL) {
-        const int j = j0 + sub;
-        float kf[8];
+      constexpr int kXR = F32 ? 1 : kXRounds;
+    // rounds past kPreTail tokens, kXR at a time: their keys are read as
+      // the prefetched ones (clamped rows, whole 16-byte pieces, no branch), the
+      // rounds' loads in flight together
+      for (int j0 = 4 * wave + 4 * kWavesL * kKtRounds; j0 < T; j0 += 4 * kWavesL * kXR) {
+        uint4 kr[kXR][2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-          kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
-        tail_scores(j, kf);
+        for (int x = 0; x < kXR; ++x) {
+          const size_t e = ((size_t)unit * T + max(min(j0 + 4 * kWavesL * x + sub, T - 1), 0)) * 128 + 8 * cl;
+          if constexpr (F32) {
+            const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+            kr[x][0] = cqd::ld_nt(src);
+            kr[x][1] = cqd::ld_nt(src + 1);
+          } else {
+            kr[x][0] = cqd::ld_nt(reinterpret_cast<const __half*>(ktb) + e);
+            kr[x][1] = make_uint4(0, 0, 0, 0);
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < kXR; ++x) {
+          float kf[8];
+          if constexpr (F32) {
+            kf[0] = __uint_as_float(kr[x][0].x); kf[1] = __uint_as_float(kr[x][0].y);
+            kf[2] = __uint_as_float(kr[x][0].z); kf[3] = __uint_as_float(kr[x][0].w);
+            kf[4] = __uint_as_float(kr[x][1].x); kf[5] = __uint_as_float(kr[x][1].y);
+            kf[6] = __uint_as_float(kr[x][1].z); kf[7] = __uint_as_float(kr[x][1].w);
+          } else {
+            const uint32_t hw[4] = {kr[x][0].x, kr[x][0].y, kr[x][0].z, kr[x][0].w};
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+              kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+            }
+          }
+          tail_scores(j0 + 4 * kWavesL * x + sub, kf);          // rows past T: scores not stored
+        }
       }
     }
 
@@ -1268,13 +1355,40 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
           ta[hh][1] = fmaf(w, v1, ta[hh][1]);
         }
       }
-      for (int t = kPreTail + vph; t < T; t += kPhases) {
-        const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
-        const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
+      constexpr int kXT = F32 ? 4 : kXTokens;
+    // tokens past kPreTail, kXT at a time: loads in flight together
+      // (clamped rows, no branch); a token past T weighs 0
+      for (int t0 = kPreTail + vph; t0 < T; t0 += kPhases * kXT) {
+        uint32_t vx[kXT][F32 ? 2 : 1];
 #pragma unroll
-        for (int hh = 0; hh < G; ++hh) {
-          ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-          ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+        for (int x = 0; x < kXT; ++x) {
+          const size_t e = ((size_t)unit * T + max(min(t0 + kPhases * x, T - 1), 0)) * 128 + 2 * vcp;
+          if constexpr (F32) {
+            const uint2 w2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+            vx[x][0] = w2.x;
+            vx[x][F32 ? 1 : 0] = w2.y;
+          } else {
+            vx[x][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
+          }
+        }
+#pragma unroll
+        for (int x = 0; x < kXT; ++x) {
+          const int t = t0 + kPhases * x;
+          const bool tok = t < T;
+          float v0, v1;
+          if constexpr (F32) {
+            v0 = __uint_as_float(vx[x][0]);
+            v1 = __uint_as_float(vx[x][F32 ? 1 : 0]);
+          } else {
+            v0 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] & 0xFFFF)));
+            v1 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] >> 16)));
+          }
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) {
+            const float w = tok ? s_ts[hh][min(t, kMaxTail - 1)] : 0.f;
+            ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+            ta[hh][1] = fmaf(w, v1, ta[hh][1]);
+          }
         }
       }
 #pragma unroll
@@ -1673,13 +1787,42 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
       }
       tail_scores(4 * wave + 4 * kWaves * r + sub, kf);
     }
-    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves) {
-      const int j = j0 + sub;
-      float kf[8];
+    constexpr int kXR = F32 ? 1 : kXRounds;
+    // rounds past kPreTail tokens, kXR at a time: their keys are read as
+    // the prefetched ones (clamped rows, whole 16-byte pieces, no branch), the
+    // rounds' loads in flight together
+    for (int j0 = 4 * wave + 4 * kWaves * kKtRounds; j0 < Tf; j0 += 4 * kWaves * kXR) {
+      uint4 kr[kXR][2];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        kf[c] = j < T ? ld_any(P.kt, ((size_t)unit * T + j) * 128 + 8 * cl + c, F32) : 0.f;
-      tail_scores(j, kf);
+      for (int x = 0; x < kXR; ++x) {
+        const size_t e = ((size_t)unit * T + max(min(j0 + 4 * kWaves * x + sub, T - 1), 0)) * 128 + 8 * cl;
+        if constexpr (F32) {
+          const uint4* src = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(ktb) + e);
+          kr[x][0] = cqd::ld_nt(src);
+          kr[x][1] = cqd::ld_nt(src + 1);
+        } else {
+          kr[x][0] = cqd::ld_nt(reinterpret_cast<const __half*>(ktb) + e);
+          kr[x][1] = make_uint4(0, 0, 0, 0);
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kXR; ++x) {
+        float kf[8];
+        if constexpr (F32) {
+          kf[0] = __uint_as_float(kr[x][0].x); kf[1] = __uint_as_float(kr[x][0].y);
+          kf[2] = __uint_as_float(kr[x][0].z); kf[3] = __uint_as_float(kr[x][0].w);
+          kf[4] = __uint_as_float(kr[x][1].x); kf[5] = __uint_as_float(kr[x][1].y);
+          kf[6] = __uint_as_float(kr[x][1].z); kf[7] = __uint_as_float(kr[x][1].w);
+        } else {
+          const uint32_t hw[4] = {kr[x][0].x, kr[x][0].y, kr[x][0].z, kr[x][0].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(hw[c] & 0xFFFF)));
+            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(hw[c] >> 16)));
+          }
+        }
+        tail_scores(j0 + 4 * kWaves * x + sub, kf);          // rows past T: scores not stored
+      }
     }
   }
   // ---- min / max of every head's visual scores ---------------------------
@@ -1754,13 +1897,40 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
         ta[hh][1] = fmaf(w, v1, ta[hh][1]);
       }
     }
-    for (int t = kPreTail + vph; t < Tf; t += kPhases) {
-      const float v0 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp, F32);
-      const float v1 = ld_any(P.vt, ((size_t)unit * T + t) * 128 + 2 * vcp + 1, F32);
+    constexpr int kXT = F32 ? 4 : kXTokens;
+    // tokens past kPreTail, kXT at a time: loads in flight together
+    // (clamped rows, no branch); a token past T weighs 0
+    for (int t0 = kPreTail + vph; t0 < Tf; t0 += kPhases * kXT) {
+      uint32_t vx[kXT][F32 ? 2 : 1];
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        ta[hh][0] = fmaf(s_ts[hh][t], v0, ta[hh][0]);
-        ta[hh][1] = fmaf(s_ts[hh][t], v1, ta[hh][1]);
+      for (int x = 0; x < kXT; ++x) {
+        const size_t e = ((size_t)unit * T + max(min(t0 + kPhases * x, T - 1), 0)) * 128 + 2 * vcp;
+        if constexpr (F32) {
+          const uint2 w2 = *reinterpret_cast<const uint2*>(reinterpret_cast<const float*>(vtb) + e);
+          vx[x][0] = w2.x;
+          vx[x][F32 ? 1 : 0] = w2.y;
+        } else {
+          vx[x][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(reinterpret_cast<const __half*>(vtb) + e));
+        }
+      }
+#pragma unroll
+      for (int x = 0; x < kXT; ++x) {
+        const int t = t0 + kPhases * x;
+        const bool tok = t < Tf;
+        float v0, v1;
+        if constexpr (F32) {
+          v0 = __uint_as_float(vx[x][0]);
+          v1 = __uint_as_float(vx[x][F32 ? 1 : 0]);
+        } else {
+          v0 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] & 0xFFFF)));
+          v1 = __half2float(__ushort_as_half((unsigned short)(vx[x][0] >> 16)));
+        }
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          const float w = tok ? s_ts[hh][min(t, kMaxTail - 1)] : 0.f;
+          ta[hh][0] = fmaf(w, v0, ta[hh][0]);
+          ta[hh][1] = fmaf(w, v1, ta[hh][1]);
+        }
       }
     }
 #pragma unroll
