@@ -174,33 +174,54 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
         vr[i][0] = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(vtb + e * 2));
       }
     }
+    // the chunk's key rounds, kLR at a time with their loads in flight
+    // together; the heads' sums of a round side by side
+    constexpr int kLR = F32 ? 1 : 4;
 #pragma unroll
-    for (int r = 0; r < kRounds; ++r) {
-      const int j = c0 + 4 * wave + sub + 4 * kWaves * r;
-      const size_t e = ((size_t)unit * T + min(j, T - 1)) * 128 + 8 * cl;
-      float kf[8];
-      if constexpr (F32) {
-        const uint4* src = reinterpret_cast<const uint4*>(ktb + e * 4);
-        const uint4 x0 = cqd::ld_nt(src), x1 = cqd::ld_nt(src + 1);
-        const uint32_t w[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+    for (int r0 = 0; r0 < kRounds; r0 += kLR) {
+      uint4 kr[kLR][2];
 #pragma unroll
-        for (int c = 0; c < 8; ++c) kf[c] = __uint_as_float(w[c]);
-      } else {
-        const uint4 x = cqd::ld_nt(reinterpret_cast<const __half*>(ktb + e * 2));
-        const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(w[c] & 0xFFFF)));
-          kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(w[c] >> 16)));
+      for (int x = 0; x < kLR; ++x) {
+        const int j = c0 + 4 * wave + sub + 4 * kWaves * (r0 + x);
+        const size_t e = ((size_t)unit * T + min(j, T - 1)) * 128 + 8 * cl;
+        if constexpr (F32) {
+          const uint4* src = reinterpret_cast<const uint4*>(ktb + e * 4);
+          kr[x][0] = cqd::ld_nt(src);
+          kr[x][1] = cqd::ld_nt(src + 1);
+        } else {
+          kr[x][0] = cqd::ld_nt(reinterpret_cast<const __half*>(ktb + e * 2));
+          kr[x][1] = make_uint4(0, 0, 0, 0);
         }
       }
 #pragma unroll
-      for (int hh = 0; hh < G; ++hh) {
-        float sc = 0.f;
+      for (int x = 0; x < kLR; ++x) {
+        const int j = c0 + 4 * wave + sub + 4 * kWaves * (r0 + x);
+        float kf[8];
+        if constexpr (F32) {
+          const uint32_t w[8] = {kr[x][0].x, kr[x][0].y, kr[x][0].z, kr[x][0].w,
+                                 kr[x][1].x, kr[x][1].y, kr[x][1].z, kr[x][1].w};
 #pragma unroll
-        for (int c = 0; c < 8; ++c) sc = fmaf(s_q[hh][8 * cl + c], kf[c], sc);
-        sc = cqm::row_sum16(sc);
-        if (cl == 0) s_ts[hh][j - c0] = j < T ? sc : -INFINITY;
+          for (int c = 0; c < 8; ++c) kf[c] = __uint_as_float(w[c]);
+        } else {
+          const uint32_t w[4] = {kr[x][0].x, kr[x][0].y, kr[x][0].z, kr[x][0].w};
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            kf[2 * c] = __half2float(__ushort_as_half((unsigned short)(w[c] & 0xFFFF)));
+            kf[2 * c + 1] = __half2float(__ushort_as_half((unsigned short)(w[c] >> 16)));
+          }
+        }
+        float sc[G];
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          sc[hh] = 0.f;
+#pragma unroll
+          for (int c = 0; c < 8; ++c) sc[hh] = fmaf(s_q[hh][8 * cl + c], kf[c], sc[hh]);
+        }
+        cqm::row_sum16x(sc);
+        if (cl == 0) {
+#pragma unroll
+          for (int hh = 0; hh < G; ++hh) s_ts[hh][j - c0] = j < T ? sc[hh] : -INFINITY;
+        }
       }
     }
     cqm::lds_barrier();
