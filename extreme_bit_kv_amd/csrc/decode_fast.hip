@@ -136,14 +136,17 @@ struct Params {
   int nc;               // token capacity of the code buffers (their layout is that of nc >= n tokens)
 };
 
-// A text tail longer than the fused pass takes (T > kMaxTail), for one unit,
-// run by the 8 waves of its workgroup after its visual sums are done, in
-// chunks of kMaxTail tokens with a running reference (online softmax):
+// The part of a text tail beyond the fused pass's kMaxTail tokens (T >
+// kMaxTail), for one unit, run by the 8 waves of its workgroup after its
+// visual sums are done, in chunks of kMaxTail tokens with a running reference
+// (online softmax):
 //   m = max_t s_t so far;  acc = sum_t exp(s_t - m) vt_t;  pt = sum_t exp(s_t - m),
 // rescaled by exp(m_old - m_new) when a chunk raises m (the text tail is not
 // quantized: "Method" part 2 applies to the visual cache only, per the
-// abstract).  Leaves sum_t exp(s_t - m) vt_t per (phase, head, channel) in
-// s_tailred, the sums in s_ptail and m in s_tm.  Chunk scores: thread (token
+// abstract).  It starts from the fused pass's first kMaxTail tokens (their
+// sums per (phase, head, channel) in s_tailred, relative to the reference in
+// s_tm, their weight in s_ptail) and leaves sum_t exp(s_t - m) vt_t over all
+// T tokens in s_tailred, the sums in s_ptail and m in s_tm.  Chunk scores: thread (token
 // 4 wave + lane / 16 + 32 r, channels 8 (lane % 16) ..); chunk values: thread
 // (channel pair tid % 64, tokens tid / 64 + 8 i).
 template <int G, bool F32>
@@ -159,7 +162,14 @@ __device__ void long_tail(const Params& P, int unit, const float (&s_q)[4][128],
   const char* vtb = reinterpret_cast<const char*>(P.vt);
   float m_run[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY}, pt[4] = {0.f, 0.f, 0.f, 0.f};
   float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-  for (int c0 = 0; c0 < T; c0 += kMaxTail) {
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {                 // the fused pass's first kMaxTail tokens
+    m_run[hh] = s_tm[hh];
+    pt[hh] = s_ptail[hh];
+    ta[hh][0] = s_tailred[vph][hh][2 * vcp];
+    ta[hh][1] = s_tailred[vph][hh][2 * vcp + 1];
+  }
+  for (int c0 = kMaxTail; c0 < T; c0 += kMaxTail) {
     // this chunk's value inputs are requested first, then its keys (rows
     // past T read the last row: clamped, and their weights are 0)
     uint32_t vr[kVals][F32 ? 2 : 1];
@@ -306,8 +316,9 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = P.n, T = P.T;
   // the text tail in the fused pass (scores beside the prologue, values
-  // beside the value pass); a longer one runs in chunks at the end
-  const int Tf = LT ? 0 : T;
+  // beside the value pass), its first kMaxTail tokens when longer: the rest
+  // runs in chunks at the end
+  const int Tf = LT ? kMaxTail : T;
   const int ntiles = (n + kTile - 1) / kTile;
   const int R = n >> 5;
   const int nc = P.nc, Rc = nc >> 5;           // the code buffers' layout: nc tokens
@@ -1566,7 +1577,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   const int b = unit / P.Hkv, h = unit % P.Hkv;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n = P.n, T = P.T;
-  const int Tf = LT ? 0 : T;                   // the text tail in the fused pass (else chunked at the end)
+  const int Tf = LT ? kMaxTail : T;            // the text tail in the fused pass (the rest chunked at the end)
   const int tiles = (n + TB - 1) / TB;
   const int R = n / E;
   const int nc = P.nc, Rc = nc / E;            // the code buffers' layout: nc tokens
