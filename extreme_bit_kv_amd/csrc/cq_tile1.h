@@ -21,6 +21,11 @@
 
 namespace cqt {
 
+// The code words are written once and read by a later launch: their stores
+// are non-temporal, so that they do not fill the caches with dirty lines
+// (the fused quantize of K and V was 1.5 % faster with them).
+typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+
 constexpr int kWaves = 8;                    // waves per workgroup
 constexpr int kRows = 16;                    // consecutive tokens per thread
 constexpr int kTile = 4 * kWaves * kRows;    // tokens per tile (512)
@@ -120,7 +125,7 @@ __device__ __forceinline__ void store_tile_codes(const uint4 (&v)[kRows], uint32
           if (c == q)
             val = make_uint4(words[4 * (q4 + c)], words[4 * (q4 + c) + 1], words[4 * (q4 + c) + 2],
                              words[4 * (q4 + c) + 3]);
-        if (q4 + q < IT / 4) reinterpret_cast<uint4*>(dst)[q4 + q] = val;
+        if (q4 + q < IT / 4) __builtin_nontemporal_store((v4u){val.x, val.y, val.z, val.w}, reinterpret_cast<v4u*>(dst) + q4 + q);
       }
     } else if (q == 0) {
 #pragma unroll
@@ -176,8 +181,8 @@ __device__ __forceinline__ void store_tile_codes(const uint4 (&v)[kRows], uint32
     // the two halves, one instruction covers the group's 512-byte row
     if (sub < 2 && group < R_end && group < R) {
       uint32_t* dst = cu + (size_t)group * 128 + 8 * k + 4 * sub;
-      *reinterpret_cast<uint4*>(dst) = sub == 0 ? make_uint4(out[0], out[1], out[2], out[3])
-                                                : make_uint4(out[4], out[5], out[6], out[7]);
+      __builtin_nontemporal_store(sub == 0 ? (v4u){out[0], out[1], out[2], out[3]} : (v4u){out[4], out[5], out[6], out[7]},
+                                  reinterpret_cast<v4u*>(dst));
     }
   }
 }
