@@ -86,6 +86,7 @@ __device__ __align__(16) uint32_t g_pad[128];
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
 typedef unsigned int v4u __attribute__((ext_vector_type(4)));
+typedef unsigned int v2u __attribute__((ext_vector_type(2)));
 constexpr int kQMax = 15 * (31 * 31 * 31 + 31 * 31 + 31 + 1);   // largest |Q| with four base-31 digits
 constexpr int kRsrcFlags = 0x00020000;                            // raw buffer, 32-bit data format
 
@@ -1596,6 +1597,11 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ float s_tailred[kThreads / 64][4][128];
   __shared__ float s_vred[kWaves][4][128];
   __shared__ float s_psum[kWaves][4];
+  // the scores of the unit's first kKeepN tiles stay in LDS from the key pass
+  // to the value pass ([tile][lane][token]), so those key tiles are read once
+  // (as in df_b1; the rest of the LDS two workgroups per CU leave)
+  constexpr int kKeepN = BITS == 2 ? 28 : (BITS == 4 ? 66 : 140);
+  __shared__ __align__(16) float s_keepn[kKeepN][64][TPL];
 
   const int i16 = lane & 15, g4 = lane >> 4;
   const int rh = i16 >> 2, rp = i16 & 3;
@@ -1604,23 +1610,26 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   const uint32_t* vcb = n > 0 ? P.vc : g_pad;
   const char* ktb = T > 0 ? reinterpret_cast<const char*>(P.kt) : reinterpret_cast<const char*>(g_pad);
   const char* vtb = T > 0 ? reinterpret_cast<const char*>(P.vt) : reinterpret_cast<const char*>(g_pad);
-  auto load_k = [&](int tile, uint32_t (&w)[8]) {   // tokens past n: scores not used
-    const int tok0 = max(min(tile * TB + TPL * i16, n - TPL), 0);
+  // Key tiles are read with buffer loads (one descriptor per unit): a tile
+  // past the last, or a kept one in the value pass, reads out of range, which
+  // returns zeros without any traffic.  Tokens past n: scores not used.
+  const auto rk = __builtin_amdgcn_make_buffer_rsrc((void*)(kc + (n > 0 ? (size_t)unit * W * nc : 0)), (short)0,
+                                                    n > 0 ? W * nc * 4 : 0, kRsrcFlags);
+  auto load_k = [&](int tile, uint32_t (&w)[8]) {
+    const uint32_t toff = tile < tiles ? (uint32_t)(tile * TB) * 4u : 0x80000000u;
 #pragma unroll
     for (int q = 0; q < 8; ++q) w[q] = 0u;
-    {
 #pragma unroll
-      for (int p = 0; p < BITS; ++p) {
-        const uint32_t* src = kc + ((size_t)unit * W + BITS * g4 + p) * nc + tok0;
-        if constexpr (TPL == 4) {
-          const uint4 x = *reinterpret_cast<const uint4*>(src);
-          w[4 * p] = x.x; w[4 * p + 1] = x.y; w[4 * p + 2] = x.z; w[4 * p + 3] = x.w;
-        } else if constexpr (TPL == 2) {
-          const uint2 x = *reinterpret_cast<const uint2*>(src);
-          w[2 * p] = x.x; w[2 * p + 1] = x.y;
-        } else {
-          w[p] = src[0];
-        }
+    for (int p = 0; p < BITS; ++p) {
+      const uint32_t off = (uint32_t)((BITS * g4 + p) * nc + TPL * i16) * 4u + toff;
+      if constexpr (TPL == 4) {
+        const uint4 x = ld_buf(rk, off);
+        w[4 * p] = x.x; w[4 * p + 1] = x.y; w[4 * p + 2] = x.z; w[4 * p + 3] = x.w;
+      } else if constexpr (TPL == 2) {
+        const v2u x = __builtin_amdgcn_raw_buffer_load_b64(rk, (int)off, 0, 0);
+        w[2 * p] = x.x; w[2 * p + 1] = x.y;
+      } else {
+        w[p] = __builtin_amdgcn_raw_buffer_load_b32(rk, (int)off, 0, 0);
       }
     }
   };
@@ -1724,13 +1733,19 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     load_k(tile + kWaves, kn);
     // n % 32 == 0: this lane's TPL tokens are all valid or none
     const bool ok = tile * TB + TPL * i16 < n;
+    float sk[TPL];
 #pragma unroll
     for (int m = 0; m < TPL; ++m) {
       const float s = score(kw, m);
+      sk[m] = s;
       if (ok) {
         vmin = fminf(vmin, s);
         vmax = fmaxf(vmax, s);
       }
+    }
+    if (tile < kKeepN) {
+#pragma unroll
+      for (int m = 0; m < TPL; ++m) s_keepn[tile][lane][m] = sk[m];
     }
   }
   // second pass: first key and value tiles requested now (the key base goes
@@ -1755,7 +1770,7 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     }
   }
   asm("" : "+s"(kc));
-  load_k(wave, kn);
+  load_k(wave < kKeepN ? tiles : wave, kn);     // a kept tile: an out-of-range read, no traffic
   auto load_v = [&](int tile, uint32_t (&w)[8]) {   // rows past the last: p = 0 (as in df_b1)
     const int row = max(min(tile * 4 + g4, R - 1), 0);
     const uint4* src = reinterpret_cast<const uint4*>(vcb + ((size_t)unit * Rc + row) * 128 + 8 * i16);
@@ -1988,7 +2003,8 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     }
     // (b = 8: the next key tile is requested once this one's scores are done,
     // which keeps both key tiles from being live at once)
-    if constexpr (BITS < 8) load_k(tile + kWaves, kn);
+    const int knext = tile + kWaves < kKeepN ? tiles : tile + kWaves;   // kept: no traffic
+    if constexpr (BITS < 8) load_k(knext, kn);
     load_v(tile + kWaves, vn);
     const bool ok = oh < G && tile * TB + TPL * i16 < n;
     // p relative to the largest visual probability, as four signed digits of
@@ -1996,13 +2012,13 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
     uint32_t fb[TPL];
 #pragma unroll
     for (int m = 0; m < TPL; ++m) {
-      const float s = score(kw, m);
+      const float s = tile < kKeepN ? s_keepn[tile][lane][m] : score(kw, m);
       float p = 0.f;
       if (ok) p = exp2f(fmaf(s, lam2, mu2));
       psum += p;
       fb[m] = cqm::sdigits(cqm::p_fixed(p));
     }
-    if constexpr (BITS == 8) load_k(tile + kWaves, kn);
+    if constexpr (BITS == 8) load_k(knext, kn);
     if (oh < G) {
 #pragma unroll
       for (int pl = 0; pl < 4; ++pl) {
