@@ -7,6 +7,8 @@ so that the scratch left by the first call cannot leak into the second.  The
 small case of each schedule is also checked against the oracle to the decode
 tolerance (QbitAI article on CalibQuant, "Method" parts 2 and 3).
 """
+import gc
+
 import numpy as np
 import pytest
 
@@ -37,10 +39,19 @@ def _both(args, n, bits, path, calib, splits=0):
                              out_dtype=torch.float32)
     out = torch.full(q.shape, float("nan"), dtype=torch.float32, device=q.device)
     torch.cuda.synchronize()
-    before = torch.cuda.memory_allocated()
-    cqb.cq_decode_attn_noalloc(*args, n=n, bits=bits, sm_scale=SM, calib=calib, path=path, splits=splits, out=out)
-    torch.cuda.synchronize()
-    assert torch.cuda.memory_allocated() == before
+    # the collector could free an earlier test's tensors in the middle of the
+    # call and make the count drop: collect first, and keep it off meanwhile
+    gc.collect()
+    gc.disable()
+    try:
+        before = torch.cuda.memory_allocated()
+        cqb.cq_decode_attn_noalloc(*args, n=n, bits=bits, sm_scale=SM, calib=calib, path=path, splits=splits,
+                                   out=out)
+        torch.cuda.synchronize()
+        after = torch.cuda.memory_allocated()
+    finally:
+        gc.enable()
+    assert after == before
     return ref, out
 
 
