@@ -1567,8 +1567,17 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 // For b = 8 a code (0..255) is not a signed byte: it enters as its low nibble
 // plus twice (8 x high nibble), three products into the same accumulator.
 // The key dot product can exceed 32 bits for b >= 4 and is summed in 64 bits.
-template <int BITS, int G, bool F32, bool LT>
-__global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
+// the key tiles whose scores stay in LDS: as many as two workgroups per CU
+// leave room for, or (ALL) those of every unit of up to kAllKeepTokens tokens,
+// for launches of at most one workgroup per CU
+constexpr int kAllKeepTokens = 4096;
+template <int BITS, bool ALL>
+constexpr int keep_tiles() {
+  return ALL ? kAllKeepTokens / (128 / BITS) : (BITS == 2 ? 28 : (BITS == 4 ? 66 : 140));
+}
+
+template <int BITS, int G, bool F32, bool LT, bool ALL = false>
+__global__ void __launch_bounds__(kThreads, ALL ? 2 : 4) df_bn(Params P) {
   constexpr int E = 32 / BITS;                  // codes per word
   constexpr int TB = 4 * E;                     // tokens per tile
   constexpr int TPL = TB / 16;                  // key tokens per lane per tile
@@ -1599,8 +1608,9 @@ __global__ void __launch_bounds__(kThreads, 4) df_bn(Params P) {
   __shared__ float s_psum[kWaves][4];
   // the scores of the unit's first kKeepN tiles stay in LDS from the key pass
   // to the value pass ([tile][lane][token]), so those key tiles are read once
-  // (as in df_b1; the rest of the LDS two workgroups per CU leave)
-  constexpr int kKeepN = BITS == 2 ? 28 : (BITS == 4 ? 66 : 140);
+  // (as in df_b1; the rest of the LDS two workgroups per CU leave, or with
+  // ALL every tile of a unit of up to kAllKeepTokens tokens)
+  constexpr int kKeepN = keep_tiles<BITS, ALL>();
   __shared__ __align__(16) float s_keepn[kKeepN][64][TPL];
 
   const int i16 = lane & 15, g4 = lane >> 4;
@@ -2179,17 +2189,24 @@ hipError_t launch_l(const Params& p, int G, int units, hipStream_t st) {
   return launch_l1<4, F32>(p, units, st);
 }
 
-template <int BITS, bool F32, bool LT>
+template <int BITS, bool F32, bool LT, bool ALL>
 hipError_t launch_bn1(const Params& p, int G, int units, hipStream_t st) {
-  if (G == 1) { CQ_LAUNCH((df_bn<BITS, 1, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  if (G == 2) { CQ_LAUNCH((df_bn<BITS, 2, F32, LT>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
-  CQ_LAUNCH((df_bn<BITS, 4, F32, LT>), dim3(units), dim3(kThreads), 0, st, p);
+  if (G == 1) { CQ_LAUNCH((df_bn<BITS, 1, F32, LT, ALL>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  if (G == 2) { CQ_LAUNCH((df_bn<BITS, 2, F32, LT, ALL>), dim3(units), dim3(kThreads), 0, st, p); return hipSuccess; }
+  CQ_LAUNCH((df_bn<BITS, 4, F32, LT, ALL>), dim3(units), dim3(kThreads), 0, st, p);
   return hipSuccess;
 }
 
+// At most one unit per CU and at most kAllKeepTokens tokens: the instance that
+// keeps every tile's scores (its LDS allows one workgroup per CU, which is all
+// such a launch has), so no key tile is read twice.  The scores are the same
+// values either way, so are the outputs.
 template <int BITS, bool F32>
 hipError_t launch_bn(const Params& p, int G, int units, hipStream_t st) {
-  return p.T > kMaxTail ? launch_bn1<BITS, F32, true>(p, G, units, st) : launch_bn1<BITS, F32, false>(p, G, units, st);
+  if (p.T > kMaxTail) return launch_bn1<BITS, F32, true, false>(p, G, units, st);
+  const long cus = device_cus();
+  if (p.n <= kAllKeepTokens && cus > 0 && units <= cus) return launch_bn1<BITS, F32, false, true>(p, G, units, st);
+  return launch_bn1<BITS, F32, false, false>(p, G, units, st);
 }
 
 template <bool F32>

@@ -285,3 +285,20 @@ def test_fast_kernel_multibit_fp32_and_calibrated(bits):
     note(f"decode fast bits={bits} fp32 calibrated")
     got = _run(K, V, q, kt, vt, bits, RELATIVE, cqb.CQ_PATH_FAST, out_dtype=torch.float32)
     _compare(got, _oracle(K, V, q, kt, vt, bits, RELATIVE), 4)
+
+
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("n", [1024, 3328, 4096])
+def test_one_unit_per_cu_instance_equals_two_per_cu(bits, n):
+    """b = 2, 4, 8 at most one (batch, kv head) unit per CU (here 32 sequences
+    of 8 kv heads) keep every tile's scores in LDS, so no key tile is read
+    twice; more units than CUs (40 sequences) keep only the first tiles'.  The
+    scores are the same either way, so the first 32 sequences of the larger
+    batch must equal the smaller batch bit for bit, and the oracle within 2e-3."""
+    import torch
+    K, V, q, kt, vt = draw_inputs(40, 32, 8, n, 64, seed=90 + bits + n, host=False)
+    note(f"decode kept-score instances bits={bits} n={n}")
+    big = _run(K, V, q, kt, vt, bits, None)
+    small = _run(*(x[:32].contiguous() for x in (K, V, q, kt, vt)), bits, None)
+    assert np.array_equal(big[:32], small)
+    _compare(small, _oracle(K[:32], V[:32], q[:32], kt[:32], vt[:32], bits, None, [(0, 0), (31, 7)]), 4)
