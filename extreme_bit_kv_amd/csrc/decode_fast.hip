@@ -1568,9 +1568,10 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 // plus twice (8 x high nibble), three products into the same accumulator.
 // The key dot product can exceed 32 bits for b >= 4 and is summed in 64 bits.
 // the key tiles whose scores stay in LDS: as many as two workgroups per CU
-// leave room for, or (ALL) those of every unit of up to kAllKeepTokens tokens,
-// for launches of at most one workgroup per CU
-constexpr int kAllKeepTokens = 4096;
+// leave room for, or (ALL, for launches of at most one workgroup per CU) the
+// first kAllKeepTokens tokens' (108 KB of scores: with the kernel's other
+// LDS, 152 to 158 KB of the CU's 160 KB)
+constexpr int kAllKeepTokens = 6912;
 template <int BITS, bool ALL>
 constexpr int keep_tiles() {
   return ALL ? kAllKeepTokens / (128 / BITS) : (BITS == 2 ? 28 : (BITS == 4 ? 66 : 140));
@@ -1609,7 +1610,7 @@ __global__ void __launch_bounds__(kThreads, ALL ? 2 : 4) df_bn(Params P) {
   // the scores of the unit's first kKeepN tiles stay in LDS from the key pass
   // to the value pass ([tile][lane][token]), so those key tiles are read once
   // (as in df_b1; the rest of the LDS two workgroups per CU leave, or with
-  // ALL every tile of a unit of up to kAllKeepTokens tokens)
+  // ALL the tiles of the first kAllKeepTokens tokens)
   constexpr int kKeepN = keep_tiles<BITS, ALL>();
   __shared__ __align__(16) float s_keepn[kKeepN][64][TPL];
 
@@ -2197,15 +2198,15 @@ hipError_t launch_bn1(const Params& p, int G, int units, hipStream_t st) {
   return hipSuccess;
 }
 
-// At most one unit per CU and at most kAllKeepTokens tokens: the instance that
-// keeps every tile's scores (its LDS allows one workgroup per CU, which is all
-// such a launch has), so no key tile is read twice.  The scores are the same
-// values either way, so are the outputs.
+// At most one unit per CU: the instance that keeps the scores of the first
+// kAllKeepTokens tokens (its LDS allows one workgroup per CU, which is all
+// such a launch has), so only the key tiles past them are read twice.  The
+// scores are the same values either way, so are the outputs.
 template <int BITS, bool F32>
 hipError_t launch_bn(const Params& p, int G, int units, hipStream_t st) {
   if (p.T > kMaxTail) return launch_bn1<BITS, F32, true, false>(p, G, units, st);
   const long cus = device_cus();
-  if (p.n <= kAllKeepTokens && cus > 0 && units <= cus) return launch_bn1<BITS, F32, false, true>(p, G, units, st);
+  if (cus > 0 && units <= cus) return launch_bn1<BITS, F32, false, true>(p, G, units, st);
   return launch_bn1<BITS, F32, false, false>(p, G, units, st);
 }
 

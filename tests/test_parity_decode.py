@@ -288,11 +288,12 @@ def test_fast_kernel_multibit_fp32_and_calibrated(bits):
 
 
 @pytest.mark.parametrize("bits", [2, 4, 8])
-@pytest.mark.parametrize("n", [1024, 3328, 4096])
+@pytest.mark.parametrize("n", [1024, 3328, 7040, 8192])
 def test_one_unit_per_cu_instance_equals_two_per_cu(bits, n):
     """b = 2, 4, 8 at most one (batch, kv head) unit per CU (here 32 sequences
-    of 8 kv heads) keep every tile's scores in LDS, so no key tile is read
-    twice; more units than CUs (40 sequences) keep only the first tiles'.  The
+    of 8 kv heads) keep the scores of the first 6912 tokens in LDS, so only
+    the key tiles past them are read twice; more units than CUs (40
+    sequences) keep fewer (1792 / 2112 / 2240 tokens at b = 2 / 4 / 8).  The
     scores are the same either way, so the first 32 sequences of the larger
     batch must equal the smaller batch bit for bit, and the oracle within 2e-3."""
     import torch
