@@ -2198,15 +2198,20 @@ hipError_t launch_bn1(const Params& p, int G, int units, hipStream_t st) {
   return hipSuccess;
 }
 
-// At most one unit per CU: the instance that keeps the scores of the first
-// kAllKeepTokens tokens (its LDS allows one workgroup per CU, which is all
-// such a launch has), so only the key tiles past them are read twice.  The
+// The instance that keeps the scores of the first kAllKeepTokens tokens (its
+// LDS allows one workgroup per CU) reads only the key tiles past them twice.
+// It is the faster one at most one unit per CU, which is all such a launch
+// has, and, although it then runs the units in rounds, on long caches, where
+// the two-per-CU instance would read most key tiles twice (measured on
+// MI355X, 32q/8kv, 512 to 1024 units: 8 to 19 % faster from 4096 tokens at
+// b = 4 and 8, 1 to 4 % from 6144 at b = 2; 7 to 13 % slower at 3328).  The
 // scores are the same values either way, so are the outputs.
 template <int BITS, bool F32>
 hipError_t launch_bn(const Params& p, int G, int units, hipStream_t st) {
   if (p.T > kMaxTail) return launch_bn1<BITS, F32, true, false>(p, G, units, st);
   const long cus = device_cus();
-  if (cus > 0 && units <= cus) return launch_bn1<BITS, F32, false, true>(p, G, units, st);
+  if ((cus > 0 && units <= cus) || p.n >= (BITS == 2 ? 6144 : 4096))
+    return launch_bn1<BITS, F32, false, true>(p, G, units, st);
   return launch_bn1<BITS, F32, false, false>(p, G, units, st);
 }
 

@@ -293,9 +293,11 @@ def test_one_unit_per_cu_instance_equals_two_per_cu(bits, n):
     """b = 2, 4, 8 at most one (batch, kv head) unit per CU (here 32 sequences
     of 8 kv heads) keep the scores of the first 6912 tokens in LDS, so only
     the key tiles past them are read twice; more units than CUs (40
-    sequences) keep fewer (1792 / 2112 / 2240 tokens at b = 2 / 4 / 8).  The
-    scores are the same either way, so the first 32 sequences of the larger
-    batch must equal the smaller batch bit for bit, and the oracle within 2e-3."""
+    sequences) keep fewer (1792 / 2112 / 2240 tokens at b = 2 / 4 / 8) on
+    caches shorter than 4096 tokens (6144 at b = 2), and the same 6912 on
+    longer ones.  The scores are the same either way, so the first 32
+    sequences of the larger batch must equal the smaller batch bit for bit,
+    and the oracle within 2e-3."""
     import torch
     K, V, q, kt, vt = draw_inputs(40, 32, 8, n, 64, seed=90 + bits + n, host=False)
     note(f"decode kept-score instances bits={bits} n={n}")
