@@ -94,7 +94,13 @@ typedef struct {
  * else the LDS-score one; otherwise the split one below 64 units, else the
  * one-launch one.  The FAST_ values force one (decode only; for quantization
  * they mean CQ_PATH_FAST):
- *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head);
+ *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head); it
+ *                       keeps the scores of a unit's first key tiles in LDS
+ *                       for the value pass and reads the other key tiles
+ *                       again (at b > 1 those of the first 6912 tokens when
+ *                       there is at most one unit per CU or n >= 4096, 6144
+ *                       at b = 2, one workgroup per CU; fewer otherwise, two
+ *                       per CU); the results do not depend on which;
  *   CQ_PATH_FAST_SPLIT  b = 1 only: a key-pass launch and a value-pass launch,
  *                       each over token chunks of every (batch, kv head);
  *   CQ_PATH_FAST_LDS    b = 1 only, G * ceil(n/128) <= 256 (n <= 8192 at
