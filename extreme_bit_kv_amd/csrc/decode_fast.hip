@@ -339,7 +339,10 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
   __shared__ float s_vmax[4], s_tm[4], s_cm[4], s_cs[4];   // visual max, tail reference; long-tail chunk max / sum
-  __shared__ float s_tailred[kThreads / 64][4][128];   // tail values per token phase
+  // dealt tiles, text tail up to kMaxTail: the tail-value sums stay in registers
+  // through the value pass (then in s_pdig), which leaves room for more kept scores
+  constexpr bool kRegTail = TPW == 0 && !LT;
+  __shared__ float s_tailred[kRegTail ? 1 : kThreads / 64][4][128];   // tail values per token phase
   __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
   __shared__ int s_next[2];                        // next key tile of each pass
@@ -349,7 +352,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   // so those key tiles are read once; the others are read again and their
   // scores recomputed (same operations, so the same values).  kKeep fills
   // the LDS that two workgroups per CU leave.
-  constexpr int kKeep = TPW == 0 ? 17 : 0;
+  constexpr int kKeep = TPW == 0 ? (kRegTail ? 25 : 17) : 0;
   __shared__ __align__(16) float s_keep[kKeep > 0 ? kKeep : 1][64][8];
 
   // operand coordinates of the 16 x 16 x 64 products
@@ -757,8 +760,8 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   lds_barrier();
   // text-tail values: thread (channel pair vcp, phase vph) sums the tail
   // tokens vph + kPhases i for every head, the first kPreTail from the loads above
+  float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
   {
-    float ta[4][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
 #pragma unroll
     for (int i = 0; i < kPreTail / kPhases; ++i) {
       // (a select, not a branch: a token past T weighs 0, and the heads'
@@ -816,10 +819,12 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
         }
       }
     }
+    if constexpr (!kRegTail) {
 #pragma unroll
-    for (int hh = 0; hh < G; ++hh) {
-      s_tailred[vph][hh][2 * vcp] = ta[hh][0];
-      s_tailred[vph][hh][2 * vcp + 1] = ta[hh][1];
+      for (int hh = 0; hh < G; ++hh) {
+        s_tailred[vph][hh][2 * vcp] = ta[hh][0];
+        s_tailred[vph][hh][2 * vcp + 1] = ta[hh][1];
+      }
     }
   }
 
@@ -931,6 +936,15 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   flush();
   psum = cqm::row_sum16(psum);
   if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
+  float* tr = reinterpret_cast<float*>(&s_pdig[0][0][0][0]);   // [phase][head][channel] once the values are done
+  if constexpr (kRegTail) {
+    // phase vph is this wave: its slot of s_pdig, which no other wave uses
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      tr[(vph * 4 + hh) * 128 + 2 * vcp] = ta[hh][0];
+      tr[(vph * 4 + hh) * 128 + 2 * vcp + 1] = ta[hh][1];
+    }
+  }
   lds_barrier();
   if constexpr (LT) {
     long_tail<G, F32>(P, unit, s_q, s_ts, s_tailred, s_ptail, s_tm, s_cm, s_cs);
@@ -942,7 +956,7 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     const float pv = (float)(s_psum[hh] * (1.0 / 134217728.0));                       // 2^-27
     float tail = 0.f;
 #pragma unroll
-    for (int q = 0; q < kPhases; ++q) tail += s_tailred[q][hh][j];
+    for (int q = 0; q < kPhases; ++q) tail += kRegTail ? tr[(q * 4 + hh) * 128 + j] : s_tailred[q][hh][j];
     const float pt = s_ptail[hh];
     // the visual sums are relative to the largest visual weight, the tail's
     // to its reference (top in the fused pass, the tail's own largest score
