@@ -441,13 +441,14 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
       }
     }
   };
-  // the key pass keeps two tiles of look-ahead per wave (kn, km), the value
-  // pass one (kn, vn); the first two are requested under the prologue.  With
+  // the key pass keeps two tiles of look-ahead per wave (a ring of three
+  // tile slots: kn, km, kx), the value pass one (kn, vn); the first two are
+  // requested under the prologue.  With
   // TPW > 0 every key tile of the wave is requested here, and the tail values
   // and value tiles right after the prologue (issued together with these, they
   // would delay the prologue's own inputs, which queue behind every CU's
   // requests).
-  uint4 kn0, kn1, km0, km1;
+  uint4 kn0, kn1, km0, km1, kx0, kx1;
   constexpr int kSlots = TPW > 0 ? TPW : 1;
   uint4 kwide[kSlots][2], vwide[kSlots][2];
   if constexpr (TPW > 0) {
@@ -666,19 +667,21 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
       }
     }
   }
-  // a wave's tiles come in increasing order: tile, then tnext (loading into
-  // km), then nxt
-  for (int tile = wave, tnext = wave + kWaves; TPW == 0 && tile < ntiles;) {
+  // a wave's tiles come in increasing order.  The ring's slots keep their
+  // roles through an unrolled round of three steps: a step requests the next
+  // tile into the free slot and scores the oldest one, so two tiles stay in
+  // flight while one is scored.  (Copying a slot into another would wait for
+  // the load still in flight into it: one tile of look-ahead.)
+  auto key_step = [&](const uint4& w0, const uint4& w1, int tile, uint4& f0, uint4& f1, int& tf)
+                      __attribute__((always_inline)) {
     int nxt = 0;
     if (lane == 0) nxt = atomicAdd(&s_next[0], 1);
     nxt = __builtin_amdgcn_readfirstlane(nxt);
-    const uint4 kw0 = kn0, kw1 = kn1;
-    kn0 = km0;
-    kn1 = km1;
-    load_k(nxt, km0, km1);                      // past the last tile: an in-bounds reread, unused
+    load_k(nxt, f0, f1);                        // past the last tile: an out-of-range read, unused
+    tf = nxt;
     // n % 32 == 0, so this lane's 8 tokens tile*128 + 8 i16 + m are all valid or none
     float st[8];
-    scores(kw0, kw1, st);
+    scores(w0, w1, st);
     if ((tile + 1) * kTile <= n || tile * kTile + 8 * i16 < n) {
       vmin = min3f(min3f(vmin, st[0], st[1]), min3f(st[2], st[3], st[4]), min3f(st[5], st[6], st[7]));
       vmax = max3f(max3f(vmax, st[0], st[1]), max3f(st[2], st[3], st[4]), max3f(st[5], st[6], st[7]));
@@ -691,8 +694,16 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     // fold tile by tile: left free, the compiler sinks these updates past the
     // loop and keeps every tile's scores alive
     asm volatile("" : "+v"(vmin), "+v"(vmax));
-    tile = tnext;
-    tnext = nxt;
+  };
+  if constexpr (TPW == 0) {
+    int ta = wave, tb = wave + kWaves, tx = ntiles;
+    while (ta < ntiles) {
+      key_step(kn0, kn1, ta, kx0, kx1, tx);
+      if (tb >= ntiles) break;
+      key_step(km0, km1, tb, kn0, kn1, ta);
+      if (tx >= ntiles) break;
+      key_step(kx0, kx1, tx, km0, km1, tb);
+    }
   }
   // the first key and value tiles of the second pass, then the first
   // kPreTail tail values, are requested before the score statistics settle.
