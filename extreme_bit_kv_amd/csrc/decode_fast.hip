@@ -334,15 +334,19 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   __shared__ int s_F[4];
   __shared__ __align__(16) uint32_t s_adig[4][4][32];   // K-side fp6 digit codes: [head][plane][128 k slots]
   __shared__ float s_kc[4];                              // per head: sum of Q / 8 over the bit-3 channels
-  __shared__ __align__(16) uint32_t s_pdig[kWaves][4][4][32];   // V-side A digits: [head][plane][128 token bytes]
+  // V-side A digits, [head][plane][128 token bytes] per wave: with dealt
+  // tiles they go to the wave's home slot of s_keep instead (below)
+  __shared__ __align__(16) uint32_t s_pdig[TPW > 0 ? kWaves : 1][4][4][32];
   __shared__ float s_ts[4][kMaxTail];           // tail scores, then tail probabilities
   __shared__ float s_red[kWaves][4][2];
   __shared__ float s_lam[4], s_mu[4], s_ptail[4], s_alpha[4];
   __shared__ float s_vmax[4], s_tm[4], s_cm[4], s_cs[4];   // visual max, tail reference; long-tail chunk max / sum
   // dealt tiles, text tail up to kMaxTail: the tail-value sums stay in registers
-  // through the value pass (then in s_pdig), which leaves room for more kept scores
+  // through the value pass (then in the home slots of s_keep), which leaves
+  // room for more kept scores
   constexpr bool kRegTail = TPW == 0 && !LT;
-  __shared__ float s_tailred[kRegTail ? 1 : kThreads / 64][4][128];   // tail values per token phase
+  constexpr int kTR = kRegTail ? 1 : kThreads / 64, kTH = kRegTail ? 1 : 4, kTC = kRegTail ? 1 : 128;
+  __shared__ float s_tailred[kTR][kTH][kTC];   // tail values per token phase (unused with kRegTail)
   __shared__ unsigned long long s_vsum[4][128];   // sum 2^7 P c per head and channel (2^-29 units)
   __shared__ double s_psum[4];                     // sum P per head (2^-22 units)
   __shared__ int s_next[2];                        // next key tile of each pass
@@ -351,8 +355,12 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   // the key pass to the value pass ([tile][lane][token], a lane's 8 scores),
   // so those key tiles are read once; the others are read again and their
   // scores recomputed (same operations, so the same values).  kKeep fills
-  // the LDS that two workgroups per CU leave.
-  constexpr int kKeep = TPW == 0 ? (kRegTail ? 25 : 17) : 0;
+  // the LDS that two workgroups per CU leave.  Slot w (2 KB) is also wave w's
+  // home: the value pass deals wave w tile w first, whose scores it reads
+  // before anything else, so from then on the slot holds the wave's digits
+  // of each tile (its s_pdig), and after the value pass its tail-value sums.
+  constexpr int kKeep = TPW == 0 ? (kRegTail ? 33 : 25) : 0;
+  static_assert(TPW > 0 || kKeep >= kWaves, "every wave needs a home slot");
   __shared__ __align__(16) float s_keep[kKeep > 0 ? kKeep : 1][64][8];
 
   // operand coordinates of the 16 x 16 x 64 products
@@ -866,7 +874,8 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   };
   int wtiles = 0;
   double psum = 0.0;                            // sum of this lane's P (exact: integers below 2^53)
-  unsigned char* pd = reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0]);
+  unsigned char* pd = TPW > 0 ? reinterpret_cast<unsigned char*>(&s_pdig[wave][0][0][0])
+                               : reinterpret_cast<unsigned char*>(&s_keep[wave][0][0]);
   // one value tile: probabilities of this lane's 8 tokens (head oh),
   // relative to the largest calibrated visual score, as fixed point
   // P = round(p 2^27) (tokens that do not count get exponent -inf, so p = 0),
@@ -947,9 +956,10 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   flush();
   psum = cqm::row_sum16(psum);
   if ((lane & 15) == 0 && oh < G) atomicAdd(&s_psum[oh], psum);
-  float* tr = reinterpret_cast<float*>(&s_pdig[0][0][0][0]);   // [phase][head][channel] once the values are done
+  // [phase][head][channel] once the values are done: the eight home slots
+  float* tr = reinterpret_cast<float*>(&s_keep[0][0][0]);
   if constexpr (kRegTail) {
-    // phase vph is this wave: its slot of s_pdig, which no other wave uses
+    // phase vph is this wave: its home slot, which no other wave uses
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       tr[(vph * 4 + hh) * 128 + 2 * vcp] = ta[hh][0];
@@ -967,7 +977,10 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
     const float pv = (float)(s_psum[hh] * (1.0 / 134217728.0));                       // 2^-27
     float tail = 0.f;
 #pragma unroll
-    for (int q = 0; q < kPhases; ++q) tail += kRegTail ? tr[(q * 4 + hh) * 128 + j] : s_tailred[q][hh][j];
+    for (int q = 0; q < kPhases; ++q) {
+      if constexpr (kRegTail) tail += tr[(q * 4 + hh) * 128 + j];
+      else tail += s_tailred[q][hh][j];
+    }
     const float pt = s_ptail[hh];
     // the visual sums are relative to the largest visual weight, the tail's
     // to its reference (top in the fused pass, the tail's own largest score
