@@ -60,6 +60,12 @@ __device__ __forceinline__ int bit_weight(int e) { return 3 - ((e >> 2) & 3); }
 // from rounding gives P slightly above 2^27, which every user tolerates.
 constexpr float kPOne = 134217728.f;          // 2^27
 __device__ __forceinline__ uint32_t p_fixed(float p) { return (uint32_t)fmaf(p, kPOne, 0.5f); }
+// The fixed point straight from the exponent: x27 = log2(p) + 27, so
+// 2^x27 = p 2^27, truncated: P = floor(p 2^27), one instruction fewer than
+// scaling p.  The numerator and the normalizer take the same P, and each P is
+// below p 2^27 by less than one unit (2^-27 of the largest weight).  A weight
+// of 0 (x27 = -inf) stays 0.
+__device__ __forceinline__ uint32_t p_fixed_exp2(float x27) { return (uint32_t)__builtin_amdgcn_exp2f(x27); }
 
 // Four signed base-256 digits of |x| < 2^30: the bytes of x + 0x808080 with
 // the low three offset back by 128, so x = d0 + 2^8 d1 + 2^16 d2 + 2^24 d3

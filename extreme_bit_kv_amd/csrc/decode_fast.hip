@@ -36,7 +36,7 @@
 // V side, per tile: C[16 x 16] += A[16 x 64] B[64 x 16], rows again
 // (head, plane), columns channels, contraction over tokens; B is the masked
 // V word as on the K side.  p = exp(g(s) - max) in (0, 1] becomes
-// P = round(p 2^22); token i's digits are those of P 2^(7 - s(i)), signed
+// P = floor(p 2^27); token i's digits are those of P 2^(7 - s(i)), signed
 // base 256 (the bytes of x + 0x808080, the low three offset back by 128).
 // A lane produces the digits of 8 consecutive tokens of one head, so one LDS
 // write / read pair per wave (a 4 x 4 byte transpose in registers) hands
@@ -878,17 +878,16 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
                                : reinterpret_cast<unsigned char*>(&s_keep[wave][0][0]);
   // one value tile: probabilities of this lane's 8 tokens (head oh),
   // relative to the largest calibrated visual score, as fixed point
-  // P = round(p 2^27) (tokens that do not count get exponent -inf, so p = 0),
+  // P = floor(p 2^27) (tokens that do not count get exponent -inf, so p = 0),
   // their digits through LDS to the A lanes, the products with the V words
   auto value_tile = [&](int tile, const float (&st)[8], const uint4& vw0, const uint4& vw1)
                         __attribute__((always_inline)) {
     const bool ok = oh < G && tile * kTile + 8 * i16 < n;
-    const float mu_t = ok ? mu2 : -INFINITY;
+    const float mu_t = ok ? mu2 + 27.f : -INFINITY;   // the exponent of p 2^27
     uint32_t fb[8], ptile = 0;
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
-      const float p = __builtin_amdgcn_exp2f(fmaf(st[m], lam2, mu_t));   // argument <= 0 (up to rounding)
-      const uint32_t Pm = cqm::p_fixed(p);
+      const uint32_t Pm = cqm::p_fixed_exp2(fmaf(st[m], lam2, mu_t));   // exponent <= 27 (up to rounding)
       ptile += Pm;
       fb[m] = cqm::sdigits(Pm << (m < 4 ? wt0 : wt1));   // digits of P 2^wt, |P 2^wt| <= 2^30
     }
@@ -1502,7 +1501,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
 
       uint32_t* reg = &s_sc[tile * kRegion];
       const bool ok = oh < G && tile * kTile + 8 * i16 < n;
-      const float mu_t = ok ? mu2 : -INFINITY;
+      const float mu_t = ok ? mu2 + 27.f : -INFINITY;   // the exponent of p 2^27, as in df_b1
       float st[8];
       {
         const float4* src = reinterpret_cast<const float4*>(reg + (oh < G ? oh : 0) * 128 + 8 * i16);
@@ -1513,8 +1512,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       uint32_t fb[8], ptile = 0;
 #pragma unroll
       for (int m = 0; m < 8; ++m) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(st[m], lam2, mu_t));
-        const uint32_t Pm = cqm::p_fixed(p);
+        const uint32_t Pm = cqm::p_fixed_exp2(fmaf(st[m], lam2, mu_t));
         ptile += Pm;
         fb[m] = cqm::sdigits(Pm << (m < 4 ? wt0 : wt1));
       }
