@@ -2279,10 +2279,13 @@ bool decode_wide_supported(const DecodeArgs& a) {
 // The all-in-flight instance needs a CU of its own per (batch, kv head)
 // unit: its workgroups hold half of a CU's registers, and with more units
 // than CUs the second round of workgroups would start only after the first.
+// It is chosen while at least half the CUs stay free: with a unit on nearly
+// every CU the one-launch kernel is faster (B = 32, 32q/8kv, n = 3328 on
+// MI355X: 15.7 vs 16.3 us; B = 16: 15.0 vs 14.6 us).
 bool decode_wide_preferred(const DecodeArgs& a) {
   if (!decode_wide_supported(a)) return false;
   const long cus = device_cus();
-  return cus > 0 && (long)a.B * a.Hkv <= cus;
+  return cus > 0 && 2L * a.B * a.Hkv <= cus;
 }
 
 hipError_t decode_wide(const DecodeArgs& a) {
@@ -2302,15 +2305,16 @@ bool decode_lds_supported(const DecodeArgs& a) {
 }
 
 // The automatic choice: every (batch, kv head) unit gets a workgroup, and so
-// a CU, of its own.  Measured on MI355X (b = 1, 32q/8kv): 8 to 256 units at
-// n = 3328 and 8192 are 7 to 16 % faster than the one-launch kernel and up to
-// 35 % faster than the split schedule; with two or more units per workgroup
-// the one-launch kernel, whose two workgroups per CU overlap each other's
-// phases, is faster.
+// a CU, of its own, and at least half the CUs stay free.  Measured on MI355X
+// (b = 1, 32q/8kv, n = 8192): 8 to 64 units are 1 to 3 % faster than the
+// one-launch kernel and up to 35 % faster than the split schedule, 128 units
+// equal; at 256 units (one per CU) the one-launch kernel, whose dealt tiles
+// balance the waves, is 5 % faster (24.2 vs 25.4 us), and with two or more
+// units per CU its two workgroups per CU overlap each other's phases.
 bool decode_lds_preferred(const DecodeArgs& a) {
   if (!decode_lds_supported(a)) return false;
   const long cap = lds_capacity((const void*)dl_b1<4, false>, 2);
-  return cap > 0 && (long)a.B * a.Hkv <= cap;
+  return cap > 0 && 2L * a.B * a.Hkv <= cap;
 }
 
 hipError_t decode_lds(const DecodeArgs& a) {

@@ -89,10 +89,10 @@ typedef struct {
 
 /* Execution path selection, for tests and tuning (NULL opts = automatic).
  * CQ_PATH_FAST picks one of the matrix-core decode schedules itself: at b = 1,
- * when every (batch, kv head) unit gets a workgroup (a CU) of its own (at most
- * 256 units on a 256-CU MI355X), the all-in-flight one if it takes the shape,
- * else the LDS-score one; otherwise the split one below 64 units, else the
- * one-launch one.  The FAST_ values force one (decode only; for quantization
+ * when every (batch, kv head) unit gets a CU of its own and at least half the
+ * CUs stay free (at most 128 units on a 256-CU MI355X), the all-in-flight one
+ * if it takes the shape, else the LDS-score one; otherwise the split one
+ * below 64 units, else the one-launch one.  The FAST_ values force one (decode only; for quantization
  * they mean CQ_PATH_FAST):
  *   CQ_PATH_FAST_ONE    one launch, one workgroup per (batch, kv head); it
  *                       keeps the scores of a unit's first key tiles in LDS
