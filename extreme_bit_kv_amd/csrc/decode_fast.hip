@@ -113,6 +113,14 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
+// The bit-3 fields of a key word as fp4 +-1: (w & 0x88888888) | 0x22222222,
+// written as a bit-field select so that it is one instruction (v_bfi_b32);
+// c2 holds 0x22222222 in a register (a VOP3 instruction takes no literal).
+__device__ __forceinline__ uint32_t sign_fields(uint32_t w, uint32_t c2) {
+  constexpr uint32_t m = 0x88888888u;
+  return (w & m) | (c2 & ~m);
+}
+
 __device__ __forceinline__ uint4 ld_buf(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const v4u x = __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0);
   return make_uint4(x.x, x.y, x.z, x.w);
@@ -644,13 +652,15 @@ __global__ void __launch_bounds__(kThreads, TPW > 0 ? 2 : 4) df_b1(Params P) {
   // with the 16x16x128 f8f6f4 product, A fp6 (e2m3) digits, B the key word
   // masked in place into fp4 (e2m1) fields; the plane sums are exact and the
   // same operations give the same scores in both passes
+  uint32_t kc2 = 0x22222222u;                  // in a register for sign_fields
+  asm volatile("" : "+v"(kc2));
   auto scores = [&](const uint4& w0, const uint4& w1, float (&st)[8]) {
     const uint32_t wd[8] = {w0.x, w0.y, w0.z, w0.w, w1.x, w1.y, w1.z, w1.w};
 #pragma unroll
     for (int m = 0; m < 8; ++m) {
       const uint32_t w = wd[m];
       const v8i bq{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
-                   (int)((w & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+                   (int)sign_fields(w, kc2), 0, 0, 0, 0};
       const v4f a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kdig, bq, v4f{0.f, 0.f, 0.f, 0.f}, 2, 4, 0,
                                                                       127, 0, 127);
       st[m] = fmaf(fmaf(fmaf(a[0], 31.f, a[1]), 31.f, a[2]), 31.f, a[3]);
@@ -1294,6 +1304,8 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
     int tq[kAheadK];
 #pragma unroll
     for (int j = 0; j < kAheadK; ++j) tq[j] = wave + j * kWavesL;
+    uint32_t kc2 = 0x22222222u;                // in a register for sign_fields
+    asm volatile("" : "+v"(kc2));
     auto key_tile = [&](uint4& s0, uint4& s1, int& slot_tile) {
       const int tile = slot_tile;
       int nxt = 0;
@@ -1306,7 +1318,7 @@ __global__ void __launch_bounds__(kThreadsL, 1) dl_b1(Params P, int units) {
       for (int m = 0; m < 8; ++m) {            // df_b1's scores, formed the same way
         const uint32_t w = wd[m];
         const v8i bq{(int)(w & 0x11111111u), (int)(w & 0x22222222u), (int)(w & 0x44444444u),
-                     (int)((w & 0x88888888u) | 0x22222222u), 0, 0, 0, 0};
+                     (int)sign_fields(w, kc2), 0, 0, 0, 0};
         const v4f a = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(kdig, bq, v4f{0.f, 0.f, 0.f, 0.f}, 2, 4, 0,
                                                                         127, 0, 127);
         st[m] = fmaf(fmaf(fmaf(a[0], 31.f, a[1]), 31.f, a[2]), 31.f, a[3]);
