@@ -7,8 +7,9 @@ prefill quantization of the full visual K and V caches (one cq_quantize_kv_pair
 call: both tensors in one launch) followed by one calibrated decode-attention step for every sequence
 (cq_decode_attn).  Inputs are seeded synthetic tensors already resident in HBM
 when timing starts.  W untimed steps run first, then exactly K steps are timed
-with the device synchronized on both sides; HIP events on the launch stream
-time every call.  One JSON line is printed.
+with the device synchronized on both sides and nothing recorded between the
+calls; the same K steps then run again with HIP events on the launch stream
+around every call, for the per-call times.  One JSON line is printed.
 
 Beside the step it reports the decode alone with the Infinity Cache flushed
 before each call, the float16 unquantized decode baseline over the same
@@ -289,12 +290,21 @@ def run(args):
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps)", file=sys.stderr, flush=True)
 
-    # events at step boundaries and between the two calls: a step's decode
-    # ends at the event where the next step's quantize starts, so every step
-    # carries two events (each costs a few microseconds of queue time)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    # the timed steps: nothing between the calls (an event recorded on the
+    # stream costs about 6 us of idle GPU, its release fence, so a step
+    # timed call by call would carry that twice)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        quant()
+        decode()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    wall = t1 - t0
+    # the same steps again, with events at step boundaries and between the two
+    # calls, for the split into calls (a step's decode ends at the event where
+    # the next step's quantize starts, so every step carries two events)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     ev[0].record(stream)
     for k in range(args.steps):
         quant()
@@ -302,8 +312,6 @@ def run(args):
         decode()
         ev[2 * k + 2].record(stream)
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    wall = t1 - t0
     # every quantize call completed its waits (else its codes would be
     # invalid): the last call's status word, and the header word that any
     # timed-out call since the workspace was zeroed sets
