@@ -9,7 +9,9 @@ call: both tensors in one launch) followed by one calibrated decode-attention st
 when timing starts.  W untimed steps run first, then exactly K steps are timed
 with the device synchronized on both sides and nothing recorded between the
 calls; the same K steps then run again with HIP events on the launch stream
-around every call, for the per-call times.  One JSON line is printed.
+around every call, for the per-call times (timing-only events, created
+without the system-scope fence that a default event's record performs).  One
+JSON line is printed.
 
 Beside the step it reports the decode alone with the Infinity Cache flushed
 before each call, the float16 unquantized decode baseline over the same
@@ -72,6 +74,54 @@ PROFILES = os.path.join(ROOT, "profiles")
 # ---------------------------------------------------------------------------
 # algorithmic byte counts
 # ---------------------------------------------------------------------------
+
+class TimingEvent:
+    """A HIP event for timing only, created with hipEventDisableSystemFence.
+
+    A default event's record ends with a system-scope fence (a write-back and
+    invalidation of the caches) that leaves the GPU idle for about 6 us and is
+    counted in the interval it closes; this one records its timestamp without
+    it.  Elapsed times are read only after a device synchronization.  The calls
+    go to the HIP runtime the process already loaded (torch's)."""
+    _hip = None
+    FLAGS = 0x20000000                 # hipEventDisableSystemFence
+
+    @classmethod
+    def _lib(cls):
+        if cls._hip is None:
+            import ctypes
+            path = None
+            with open("/proc/self/maps") as fh:
+                for line in fh:
+                    if "libamdhip64.so" in line:
+                        path = line.split()[-1]
+                        break
+            if path is None:
+                raise RuntimeError("the HIP runtime is not loaded (import torch and use the GPU first)")
+            cls._hip = ctypes.CDLL(path)
+        return cls._hip
+
+    def __init__(self):
+        import ctypes
+        self._c = ctypes
+        self.ev = ctypes.c_void_p()
+        if self._lib().hipEventCreateWithFlags(ctypes.byref(self.ev), ctypes.c_uint(self.FLAGS)) != 0:
+            raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def record(self, stream):
+        if self._lib().hipEventRecord(self.ev, self._c.c_void_p(stream.cuda_stream)) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_time(self, end):
+        ms = self._c.c_float()
+        if self._lib().hipEventElapsedTime(self._c.byref(ms), self.ev, end.ev) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def __del__(self):
+        if self._hip is not None and self.ev:
+            self._hip.hipEventDestroy(self.ev)
+
 
 class Flush:
     """Evicts the Infinity Cache before a cold measurement by reading 512 MiB
@@ -270,7 +320,7 @@ def run(args):
 
     if args.only == "decode":
         path = getattr(cqb, "CQ_PATH_" + args.path.upper())
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        ev = [TimingEvent() for _ in range(args.steps + 1)]
         for _ in range(args.warmup):
             decode(path)
         torch.cuda.synchronize()
@@ -298,13 +348,15 @@ def run(args):
     for k in range(args.steps):
         quant()
         decode()
+    t_enq = time.perf_counter()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     wall = t1 - t0
+    print(f"[bench] host enqueue {(t_enq - t0) * 1e3 / args.steps:.3f} ms/step", file=sys.stderr, flush=True)
     # the same steps again, with events at step boundaries and between the two
     # calls, for the split into calls (a step's decode ends at the event where
     # the next step's quantize starts, so every step carries two events)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    ev = [TimingEvent() for _ in range(2 * args.steps + 1)]
     ev[0].record(stream)
     for k in range(args.steps):
         quant()
@@ -332,7 +384,7 @@ def run(args):
     cold = []
     for _ in range(max(50, args.steps)):
         scratch()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         decode()
         b.record(stream)
@@ -350,7 +402,7 @@ def run(args):
     fcold = []
     for _ in range(max(50, args.steps)):
         scratch()
-        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a, b = TimingEvent(), TimingEvent()
         a.record(stream)
         cqb.cq_decode_attn_fp16(q, Kf, Vf, sm, out=of, workspace=fws)
         b.record(stream)
