@@ -27,9 +27,10 @@
 // D3, formed by the same operations in both passes and kept in these units
 // (the statistics take the scale 4 2^-F and the offset).  The first pass
 // over the keys only gathers every head's min and max, which fix g; the
-// value pass reads the key tiles again (they are still in the Infinity
-// Cache) and recomputes the same scores, instead of keeping 4 B per head and
-// token on chip.  Tiles are read with buffer loads: one descriptor per unit
+// scores of a unit's first key tiles wait in LDS for the value pass, which
+// reads the other key tiles again (partly from the Infinity Cache) and
+// recomputes the same scores, since keeping 4 B per head and token for every
+// tile would leave room for one workgroup per CU only.  Tiles are read with buffer loads: one descriptor per unit
 // and tensor, a fixed byte offset per lane, and a tile past the last reads
 // out of range (zeros, no traffic).
 //
