@@ -488,10 +488,10 @@ def sweeps(args):
         for _ in range(reps):
             if flush is not None:
                 flush()
-            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            a.record()
+            a, b = TimingEvent(), TimingEvent()
+            a.record(torch.cuda.current_stream())
             fn()
-            b.record()
+            b.record(torch.cuda.current_stream())
             ts.append((a, b))
         torch.cuda.synchronize()
         return float(np.median([a.elapsed_time(b) for a, b in ts])) * 1e-3
