@@ -30,7 +30,8 @@
 // scores of a unit's first key tiles wait in LDS for the value pass, which
 // reads the other key tiles again (partly from the Infinity Cache) and
 // recomputes the same scores, since keeping 4 B per head and token for every
-// tile would leave room for one workgroup per CU only.  Tiles are read with buffer loads: one descriptor per unit
+// tile would leave room for one workgroup per CU only.  Tiles are read with
+// buffer loads: one descriptor per unit
 // and tensor, a fixed byte offset per lane, and a tile past the last reads
 // out of range (zeros, no traffic).
 //
@@ -114,9 +115,9 @@ __device__ __forceinline__ float max3f(float a, float b, float c) {
   return r;
 }
 
-// The bit-3 fields of a key word as fp4 +-1: (w & 0x88888888) | 0x22222222,
-// written as a bit-field select so that it is one instruction (v_bfi_b32);
-// c2 holds 0x22222222 in a register (a VOP3 instruction takes no literal).
+// The bit-3 fields of a key word as fp4 +-1: (w & 0x88888888) | 0x22222222
+// in one instruction (v_and_or_b32, the mask in a scalar register): c2 holds
+// 0x22222222 in a vector register, since a VOP3 instruction takes no literal.
 __device__ __forceinline__ uint32_t sign_fields(uint32_t w, uint32_t c2) {
   constexpr uint32_t m = 0x88888888u;
   return (w & m) | (c2 & ~m);
